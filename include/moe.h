@@ -1,0 +1,176 @@
+/*
+ * moe.h -- C ABI of the routed Mixture-of-Experts layer for MI355X (gfx950).
+ *
+ * The layer is the "router -> resident expert -> combine" segment of MER's warm
+ * decode path (technical-overview page, "Execution architecture": warm target
+ * path GPU state -> attention -> router -> resident expert -> combine -> next
+ * layer; "Next architecture stage": GPU routing, Q4 expert execution, weighted
+ * combine).  Geometry it is tuned for: d_model 2048, d_ff 768, 128 experts,
+ * top-8 (evidence page, "Historical baseline environment", Model card).  Any
+ * d_model / d_ff that is a multiple of 32, 1 <= k <= E <= 1024, k <= 32 runs on
+ * the generic kernels.
+ *
+ * Conventions for every call
+ *  - Pointers named in the signature are DEVICE pointers unless the comment
+ *    says host.  fp32 arrays are row-major and 4-byte aligned.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  No call synchronises with the host or copies device -> host, so
+ *    data-dependent sizes (per-expert counts) stay on the device and every
+ *    call can be captured in a HIP graph.  The hidden state never re-enters
+ *    the host between calls (technical-overview page, "Target boundary").
+ *  - Ownership: the caller owns every buffer, including the workspace `ws`
+ *    (size from moe_workspace_bytes).  The library allocates no device memory
+ *    and keeps no mutable state between calls.  Two calls that share a
+ *    workspace must be stream-ordered.
+ *  - Errors: arguments are validated on the host before anything is enqueued;
+ *    on an error the call returns a status != MOE_OK and enqueues nothing.
+ *    MOE_E_HIP means a launch failed.  T == 0 is valid and enqueues nothing.
+ *  - Data preconditions checked on the device rather than the host: expert ids
+ *    outside [0, E) are dropped (the affected row contributes nothing and
+ *    expert_offsets[E] ends below T*k).
+ *
+ * Block formats (weights are "native Q8_0", evidence page, GPU-native
+ * foundation card; 4-bit experts: "Q4 expert execution", technical-overview
+ * page, Execution architecture):
+ *  - MOE_FMT_Q8_0: 34-byte blocks: fp16 scale d (little-endian) + 32 int8 q;
+ *    weight = d * q.
+ *  - MOE_FMT_Q4:   18-byte blocks: fp16 scale d + 16 bytes of nibbles, element
+ *    2i in the low nibble of byte i, 2i+1 in the high nibble; weight = d*(q-8).
+ *  A weight matrix with logical shape [in][out] is stored as `out` rows of
+ *  in/32 consecutive blocks (row n = output column n): gate and up are F rows
+ *  of D/32 blocks, down is D rows of F/32 blocks.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef int32_t moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_E_NULLPTR = 1,     /* a required pointer is NULL                          */
+  MOE_E_SHAPE = 2,       /* T < 0, D or F not a positive multiple of 32, bad k/E */
+  MOE_E_ALIGN = 3,       /* misaligned pointer or stride                         */
+  MOE_E_FORMAT = 4,      /* unknown block format or stage                        */
+  MOE_E_WORKSPACE = 5,   /* ws NULL or smaller than moe_workspace_bytes          */
+  MOE_E_UNSUPPORTED = 6, /* limits: E > 1024, k > 32, D or F > 16384              */
+  MOE_E_HIP = 7          /* a HIP launch failed                                   */
+};
+
+enum { MOE_FMT_Q8_0 = 0, MOE_FMT_Q4 = 1 };
+
+/* Stage of moe_expert_ffn. */
+enum {
+  MOE_STAGE_FULL = 0, /* in = x [T][D]: gate/up -> SwiGLU -> down                 */
+  MOE_STAGE_DOWN = 1  /* in = h [T*k][F] in flat (t, j) order: down only          */
+};
+
+/* Flags. */
+enum {
+  MOE_F_RESIDUAL = 1,      /* out += layer input                                       */
+  MOE_F_DETERMINISTIC = 2, /* fp outputs bit-reproducible run to run                   */
+  MOE_F_PRENORM = 4        /* moe_layer only: the layer input is rmsnorm(x, eps=1e-6)   */
+};
+
+/* One layer's experts (host struct holding device pointers).  Expert e's gate
+ * matrix starts at w_gate + e*gate_stride bytes, likewise up and down.  Bases
+ * and strides must be even (fp16 scales); the tuned kernels want 16-byte
+ * aligned bases, strides and row sizes and fall back to generic kernels
+ * otherwise. */
+typedef struct {
+  int32_t num_experts; /* E */
+  int32_t d_model;     /* D */
+  int32_t d_ff;        /* F */
+  int32_t format;      /* MOE_FMT_* */
+  const void* w_gate;
+  int64_t gate_stride;
+  const void* w_up;
+  int64_t up_stride;
+  const void* w_down;
+  int64_t down_stride;
+} moe_experts;
+
+/* Bytes of device workspace the calls below need for this shape (the maximum
+ * over moe_route, moe_group, moe_expert_ffn and moe_layer).  Pure host
+ * arithmetic; 0 for T == 0. */
+size_t moe_workspace_bytes(int64_t T, int32_t D, int32_t F, int32_t E, int32_t k,
+                           int32_t format, int32_t flags);
+
+/* LinearGate router (evidence page, "Layer-qualified experts" card: real
+ * LinearGate selection; top-8 in the Model card).
+ *   logits l = x G + bias, x [T][D], G [D][E] row-major, bias [E] or NULL.
+ *   topk_ids [T][k] int32: the k experts with the largest logits, ties to the
+ *     lower expert index, written in ascending id order.
+ *   topk_w [T][k] fp32: softmax over all E logits, renormalised over the
+ *     selected k (equal to the softmax of the selected logits); sums to 1.
+ * Logits are accumulated in fp32. */
+moe_status moe_route(const float* x, int64_t T, int32_t D, const float* gate, const float* bias,
+                     int32_t E, int32_t k, int32_t* topk_ids, float* topk_w, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Compact per-expert grouping (the reuse-ordering page's "existing compact
+ * expert grouping", section "What changed from the first experiment").
+ *   expert_offsets [E+1] int32: exclusive scan of per-expert counts,
+ *     expert_offsets[E] = number of valid entries (T*k).
+ *   sorted_rows [T*k] int32: flat indices t*k + j grouped by expert ascending,
+ *     ascending inside each expert (a stable sort by expert id).
+ * Integer only; identical on every run. */
+moe_status moe_group(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
+                     int32_t* expert_offsets, int32_t* sorted_rows, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Routed expert SwiGLU FFNs.
+ *   stage MOE_STAGE_FULL: in = x [T][D]; for row r = t*k + j with e = ids[t][j]:
+ *     h = silu(x_t W_gate_e) * (x_t W_up_e), y_r = h W_down_e.
+ *   stage MOE_STAGE_DOWN: in = h [T*k][F]; y_r = h_r W_down_e (the routed
+ *     down-projection operator of the reuse-ordering page, K = 768,
+ *     2,048 output rows, 128 experts, top-8).
+ *   y   [T*k][D] fp32 flat (t, j) order, or NULL;
+ *   out [T][D] fp32 = sum_j topk_w[t][j] y_{t*k+j} (+ x_t with MOE_F_RESIDUAL,
+ *     stage FULL only), or NULL.  At least one of y / out is non-NULL.
+ *   expert_offsets / sorted_rows come from moe_group on the same ids. */
+moe_status moe_expert_ffn(const float* in, int32_t stage, const moe_experts* W /* host */,
+                          const int32_t* topk_ids, const float* topk_w,
+                          const int32_t* expert_offsets, const int32_t* sorted_rows, int64_t T,
+                          int32_t k, float* y, float* out, int32_t flags, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Weighted combine (technical-overview page: "weighted combine").
+ *   out[t] = sum_{j<k} topk_w[t][j] * y[t*k+j] (+ residual[t] when non-NULL),
+ *   summed in j order.  y [T*k][D], out [T][D]. */
+moe_status moe_combine(const float* y, const float* topk_w, int64_t T, int32_t k, int32_t D,
+                       const float* residual, float* out, void* stream);
+
+/* One whole MoE layer: route -> group -> expert FFNs -> combine, enqueued with
+ * no host synchronisation (evidence page: fewer warm host synchronisations;
+ * no intermediate host re-entry).
+ *   x [T][D]; gate [D][E]; bias [E] or NULL; out [T][D].
+ *   With MOE_F_PRENORM the layer input is u = x / sqrt(mean(x^2) + 1e-6)
+ *   (the RMSNorm transition between stacked layers), else u = x; with
+ *   MOE_F_RESIDUAL out = u + MoE(u), else out = MoE(u).
+ *   topk_ids, topk_w, expert_offsets, sorted_rows: optional outputs (NULL =
+ *   kept in the workspace only). */
+moe_status moe_layer(const float* x, const float* gate, const float* bias,
+                     const moe_experts* W /* host */, int64_t T, int32_t k, int32_t flags,
+                     float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                     int32_t* sorted_rows, void* ws, size_t ws_bytes, void* stream);
+
+/* RMSNorm with unit gain (evidence page: "RMSNorm and residual transitions"):
+ * out[t] = x[t] / sqrt(mean_D(x[t]^2) + eps).  out may equal x. */
+moe_status moe_rmsnorm(const float* x, int64_t T, int32_t D, float eps, float* out, void* stream);
+
+/* Host-side helpers. */
+const char* moe_status_str(moe_status s);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

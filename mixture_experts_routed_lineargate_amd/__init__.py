@@ -1,0 +1,216 @@
+"""Python binding of libmoe_mi355x, the routed MoE layer for MI355X (gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libmoe_mi355x.so``; torch tensors supply device memory and the stream.  The
+functions carry the C ABI's names (``include/moe.h``).  There is no fallback:
+if the library is not built, importing works but the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+
+MOE_OK = 0
+FMT_Q8_0, FMT_Q4 = 0, 1
+STAGE_FULL, STAGE_DOWN = 0, 1
+F_RESIDUAL, F_DETERMINISTIC, F_PRENORM = 1, 2, 4
+BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4: 18}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({status_str(status)})")
+
+
+class moe_experts(ctypes.Structure):
+    _fields_ = [
+        ("num_experts", ctypes.c_int32), ("d_model", ctypes.c_int32),
+        ("d_ff", ctypes.c_int32), ("format", ctypes.c_int32),
+        ("w_gate", ctypes.c_void_p), ("gate_stride", ctypes.c_int64),
+        ("w_up", ctypes.c_void_p), ("up_stride", ctypes.c_int64),
+        ("w_down", ctypes.c_void_p), ("down_stride", ctypes.c_int64),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32, _I64, _SZ, _F32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_SIGS = {
+    "moe_abi_version": (_I32, []),
+    "moe_status_str": (ctypes.c_char_p, [_I32]),
+    "moe_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "moe_route": (_I32, [_P, _I64, _I32, _P, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "moe_group": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "moe_expert_ffn": (_I32, [_P, _I32, ctypes.POINTER(moe_experts), _P, _P, _P, _P, _I64, _I32,
+                              _P, _P, _I32, _P, _SZ, _P]),
+    "moe_combine": (_I32, [_P, _P, _I64, _I32, _I32, _P, _P, _P]),
+    "moe_layer": (_I32, [_P, _P, _P, ctypes.POINTER(moe_experts), _I64, _I32, _I32, _P, _P, _P,
+                         _P, _P, _P, _SZ, _P]),
+    "moe_rmsnorm": (_I32, [_P, _I64, _I32, _F32, _P, _P]),
+}
+EXPORTS = tuple(_SIGS)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_routed_lineargate_amd.build`; "
+                               "there is no non-HIP implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _need(t, dtype, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Experts:
+    """One layer's experts: device byte buffer(s) plus geometry.
+
+    ``base`` is a uint8 device tensor; expert e's gate/up/down matrices start at
+    ``base + gate_off + e*stride`` etc.
+    """
+
+    def __init__(self, base, E: int, D: int, F: int, fmt: int, stride: int,
+                 gate_off: int, up_off: int, down_off: int):
+        import torch
+        _need(base, torch.uint8, "experts")
+        self.base, self.E, self.D, self.F, self.fmt, self.stride = base, E, D, F, fmt, stride
+        p = base.data_ptr()
+        self.c = moe_experts(E, D, F, fmt, p + gate_off, stride, p + up_off, stride,
+                             p + down_off, stride)
+
+    @classmethod
+    def from_blobs(cls, blobs, D: int, F: int, fmt: int):
+        """``blobs`` uint8 [E][stride]: per expert gate rows, then up rows, then down rows."""
+        bb = BLOCK_BYTES[fmt]
+        g = F * (D // 32) * bb
+        return cls(blobs, blobs.shape[0], D, F, fmt, blobs.stride(0), 0, g, 2 * g)
+
+
+def moe_workspace_bytes(T: int, D: int, F: int, E: int, k: int, fmt: int = FMT_Q8_0,
+                        flags: int = 0) -> int:
+    return int(lib().moe_workspace_bytes(T, D, F, E, k, fmt, flags))
+
+
+def workspace(T: int, D: int, F: int, E: int, k: int, fmt: int = FMT_Q8_0, flags: int = 0,
+              device="cuda"):
+    import torch
+    n = moe_workspace_bytes(T, D, F, E, k, fmt, flags)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_route(x, gate, bias, k: int, topk_ids, topk_w, ws, stream=None):
+    import torch
+    for t, dt, n in ((x, torch.float32, "x"), (gate, torch.float32, "gate"),
+                     (bias, torch.float32, "bias"), (topk_ids, torch.int32, "topk_ids"),
+                     (topk_w, torch.float32, "topk_w"), (ws, torch.uint8, "ws")):
+        _need(t, dt, n)
+    T, D = x.shape
+    E = gate.shape[1]
+    _check("moe_route", lib().moe_route(_ptr(x), T, D, _ptr(gate), _ptr(bias), E, k,
+                                        _ptr(topk_ids), _ptr(topk_w), _ptr(ws),
+                                        0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def moe_group(topk_ids, E: int, expert_offsets, sorted_rows, ws=None, stream=None):
+    import torch
+    for t, n in ((topk_ids, "topk_ids"), (expert_offsets, "expert_offsets"),
+                 (sorted_rows, "sorted_rows")):
+        _need(t, torch.int32, n)
+    T, k = topk_ids.shape
+    _check("moe_group", lib().moe_group(_ptr(topk_ids), T, k, E, _ptr(expert_offsets),
+                                        _ptr(sorted_rows), _ptr(ws),
+                                        0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def moe_expert_ffn(inp, stage: int, experts: Experts, topk_ids, topk_w, expert_offsets,
+                   sorted_rows, y=None, out=None, flags: int = 0, ws=None, stream=None):
+    import torch
+    for t, dt, n in ((inp, torch.float32, "in"), (topk_ids, torch.int32, "topk_ids"),
+                     (topk_w, torch.float32, "topk_w"), (expert_offsets, torch.int32, "offsets"),
+                     (sorted_rows, torch.int32, "sorted_rows"), (y, torch.float32, "y"),
+                     (out, torch.float32, "out"), (ws, torch.uint8, "ws")):
+        _need(t, dt, n)
+    T, k = topk_ids.shape
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        _ptr(inp), stage, ctypes.byref(experts.c), _ptr(topk_ids), _ptr(topk_w),
+        _ptr(expert_offsets), _ptr(sorted_rows), T, k, _ptr(y), _ptr(out), flags, _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def moe_combine(y, topk_w, out, residual=None, stream=None):
+    import torch
+    for t, n in ((y, "y"), (topk_w, "topk_w"), (out, "out"), (residual, "residual")):
+        _need(t, torch.float32, n)
+    T, k = topk_w.shape
+    D = out.shape[1]
+    _check("moe_combine", lib().moe_combine(_ptr(y), _ptr(topk_w), T, k, D, _ptr(residual),
+                                            _ptr(out), _stream(stream)))
+
+
+def moe_layer(x, gate, bias, experts: Experts, k: int, out, flags: int = 0, topk_ids=None,
+              topk_w=None, expert_offsets=None, sorted_rows=None, ws=None, stream=None):
+    import torch
+    for t, dt, n in ((x, torch.float32, "x"), (gate, torch.float32, "gate"),
+                     (bias, torch.float32, "bias"), (out, torch.float32, "out"),
+                     (topk_ids, torch.int32, "topk_ids"), (topk_w, torch.float32, "topk_w"),
+                     (expert_offsets, torch.int32, "offsets"),
+                     (sorted_rows, torch.int32, "sorted_rows"), (ws, torch.uint8, "ws")):
+        _need(t, dt, n)
+    T = x.shape[0]
+    _check("moe_layer", lib().moe_layer(
+        _ptr(x), _ptr(gate), _ptr(bias), ctypes.byref(experts.c), T, k, flags, _ptr(out),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_rows), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def moe_rmsnorm(x, out, eps: float = 1e-6, stream=None):
+    import torch
+    _need(x, torch.float32, "x")
+    _need(out, torch.float32, "out")
+    T, D = x.shape
+    _check("moe_rmsnorm", lib().moe_rmsnorm(_ptr(x), T, D, eps, _ptr(out), _stream(stream)))

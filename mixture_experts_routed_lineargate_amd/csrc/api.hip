@@ -1,0 +1,270 @@
+// C ABI of libmoe_mi355x: host-side validation, workspace layout and dispatch.
+// Everything here runs on the host; every kernel is enqueued on the caller's
+// stream without synchronising.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "internal.hpp"
+
+namespace moe {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Workspace carve_workspace(void* base, int64_t T, int D, int F, int E, int k, int flags) {
+  Workspace w{};
+  const size_t tk = (size_t)T * (size_t)k;
+  const int ks = router_ksplit(T, D);
+  size_t off = 0;
+  char* b = (char*)base;
+  auto take = [&](size_t bytes) {
+    char* p = b ? b + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  w.sync = (uint32_t*)take(SYNC_BYTES);
+  w.part_logits = (float*)take((size_t)ks * (size_t)T * E * sizeof(float));
+  w.ids = (int32_t*)take(tk * sizeof(int32_t));
+  w.w = (float*)take(tk * sizeof(float));
+  w.offsets = (int32_t*)take((size_t)(E + 1) * sizeof(int32_t));
+  w.rows = (int32_t*)take(tk * sizeof(int32_t));
+  w.h = (float*)take(tk * (size_t)F * sizeof(float));
+  w.y = (float*)take(tk * (size_t)D * sizeof(float));
+  w.xn = (flags & MOE_F_PRENORM) ? (float*)take((size_t)T * D * sizeof(float)) : nullptr;
+  w.bytes = off;
+  return w;
+}
+
+bool trace_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* v = getenv("MOE_TRACE");
+    on = (v && v[0] && v[0] != '0') ? 1 : 0;
+  }
+  return on == 1;
+}
+
+void trace(const char* what, int64_t T, int D, int F, int E, int k, int fmt) {
+  if (!trace_enabled()) return;
+  fprintf(stderr, "[moe] %s T=%lld D=%d F=%d E=%d k=%d fmt=%d\n", what, (long long)T, D, F, E, k,
+          fmt);
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static moe_status check_dims(int64_t T, int D, int E, int k) {
+  if (T < 0 || D <= 0 || D % QK || E <= 0 || k <= 0 || k > E) return MOE_E_SHAPE;
+  if (E > MAX_E || k > MAX_K || D > 16384) return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
+static moe_status check_experts(const moe_experts* W) {
+  if (!W) return MOE_E_NULLPTR;
+  if (W->format != MOE_FMT_Q8_0 && W->format != MOE_FMT_Q4) return MOE_E_FORMAT;
+  if (W->d_model <= 0 || W->d_model % QK || W->d_ff <= 0 || W->d_ff % QK || W->num_experts <= 0)
+    return MOE_E_SHAPE;
+  if (W->d_model > 16384 || W->d_ff > 16384 || W->num_experts > MAX_E) return MOE_E_UNSUPPORTED;
+  if (!W->w_down) return MOE_E_NULLPTR;
+  if (!aligned(W->w_down, 2) || W->down_stride % 2 || W->down_stride < 0) return MOE_E_ALIGN;
+  return MOE_OK;
+}
+
+static moe_status check_gate_up(const moe_experts* W) {
+  if (!W->w_gate || !W->w_up) return MOE_E_NULLPTR;
+  if (!aligned(W->w_gate, 2) || !aligned(W->w_up, 2) || W->gate_stride % 2 || W->up_stride % 2 ||
+      W->gate_stride < 0 || W->up_stride < 0)
+    return MOE_E_ALIGN;
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                  \
+  do {                                 \
+    const moe_status st_ = (expr);     \
+    if (st_ != MOE_OK) return st_;     \
+  } while (0)
+
+#define HIP_TRY(expr)                         \
+  do {                                        \
+    if ((expr) != hipSuccess) return MOE_E_HIP; \
+  } while (0)
+
+// Route into the given outputs (ids / w must be device buffers of T*k).
+static moe_status do_route(const float* x, int64_t T, int D, const float* G, const float* bias,
+                           int E, int k, int32_t* ids, float* w, const Workspace& ws,
+                           hipStream_t s) {
+  const int ks = router_ksplit(T, D);
+  HIP_TRY(launch_router_partial(x, T, D, G, E, ws.part_logits, ks, s));
+  HIP_TRY(launch_topk(ws.part_logits, ks, T, E, bias, k, ids, w, s));
+  return MOE_OK;
+}
+
+static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const int32_t* ids,
+                         const float* w, const int32_t* offsets, const int32_t* rows, int64_t T,
+                         int k, float* y, float* out, int flags, const Workspace& ws,
+                         hipStream_t s) {
+  (void)offsets;
+  (void)rows;
+  const char* path = stage == MOE_STAGE_FULL ? "ffn generic gate/up+down" : "ffn generic down";
+  trace(path, T, W.D, W.F, W.E, k, W.fmt);
+  const float* h = in;
+  if (stage == MOE_STAGE_FULL) {
+    HIP_TRY(launch_gateup_generic(in, W, ids, T, k, ws.h, s));
+    h = ws.h;
+  }
+  float* ybuf = y ? y : ws.y;
+  HIP_TRY(launch_down_generic(h, W, ids, T, k, ybuf, s));
+  if (out) {
+    const float* res = (stage == MOE_STAGE_FULL && (flags & MOE_F_RESIDUAL)) ? in : nullptr;
+    HIP_TRY(launch_combine(ybuf, w, T, k, W.D, res, out, s));
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_E_NULLPTR: return "required pointer is NULL";
+    case MOE_E_SHAPE: return "invalid shape";
+    case MOE_E_ALIGN: return "misaligned pointer or stride";
+    case MOE_E_FORMAT: return "unknown block format or stage";
+    case MOE_E_WORKSPACE: return "workspace missing or too small";
+    case MOE_E_UNSUPPORTED: return "shape outside supported limits";
+    case MOE_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(int64_t T, int32_t D, int32_t F, int32_t E, int32_t k, int32_t format,
+                           int32_t flags) {
+  (void)format;
+  if (T <= 0 || D <= 0 || F <= 0 || E <= 0 || k <= 0) return 0;
+  return carve_workspace(nullptr, T, D, F, E, k, flags).bytes;
+}
+
+moe_status moe_route(const float* x, int64_t T, int32_t D, const float* gate, const float* bias,
+                     int32_t E, int32_t k, int32_t* topk_ids, float* topk_w, void* ws,
+                     size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(T, D, E, k));
+  if (T == 0) return MOE_OK;
+  if (!x || !gate || !topk_ids || !topk_w) return MOE_E_NULLPTR;
+  if (!aligned(x, 4) || !aligned(gate, 4) || (bias && !aligned(bias, 4)) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return MOE_E_ALIGN;
+  const size_t need = moe_workspace_bytes(T, D, QK, E, k, 0, 0);
+  if (!ws || ws_bytes < need) return MOE_E_WORKSPACE;
+  const Workspace w = carve_workspace(ws, T, D, QK, E, k, 0);
+  trace("route", T, D, 0, E, k, -1);
+  return do_route(x, T, D, gate, bias, E, k, topk_ids, topk_w, w, (hipStream_t)stream);
+}
+
+moe_status moe_group(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
+                     int32_t* expert_offsets, int32_t* sorted_rows, void* ws, size_t ws_bytes,
+                     void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (T < 0 || E <= 0 || k <= 0 || k > E) return MOE_E_SHAPE;
+  if (E > MAX_E || k > MAX_K) return MOE_E_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !expert_offsets || !sorted_rows) return MOE_E_NULLPTR;
+  if (!aligned(topk_ids, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_rows, 4))
+    return MOE_E_ALIGN;
+  trace("group", T, 0, 0, E, k, -1);
+  if (launch_group(topk_ids, T * k, E, expert_offsets, sorted_rows, (hipStream_t)stream) !=
+      hipSuccess)
+    return MOE_E_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const float* in, int32_t stage, const moe_experts* W,
+                          const int32_t* topk_ids, const float* topk_w,
+                          const int32_t* expert_offsets, const int32_t* sorted_rows, int64_t T,
+                          int32_t k, float* y, float* out, int32_t flags, void* ws,
+                          size_t ws_bytes, void* stream) {
+  MOE_TRY(check_experts(W));
+  if (stage != MOE_STAGE_FULL && stage != MOE_STAGE_DOWN) return MOE_E_FORMAT;
+  MOE_TRY(check_dims(T, W->d_model, W->num_experts, k));
+  if (T == 0) return MOE_OK;
+  if (stage == MOE_STAGE_FULL) MOE_TRY(check_gate_up(W));
+  if (!in || !topk_ids || !expert_offsets || !sorted_rows) return MOE_E_NULLPTR;
+  if (!y && !out) return MOE_E_NULLPTR;
+  if (out && !topk_w) return MOE_E_NULLPTR;
+  if (!aligned(in, 4) || !aligned(topk_ids, 4) || (topk_w && !aligned(topk_w, 4)) ||
+      (y && !aligned(y, 4)) || (out && !aligned(out, 4)) || !aligned(expert_offsets, 4) ||
+      !aligned(sorted_rows, 4))
+    return MOE_E_ALIGN;
+  const size_t need =
+      moe_workspace_bytes(T, W->d_model, W->d_ff, W->num_experts, k, W->format, flags);
+  if (!ws || ws_bytes < need) return MOE_E_WORKSPACE;
+  const Workspace w = carve_workspace(ws, T, W->d_model, W->d_ff, W->num_experts, k, flags);
+  return do_ffn(in, stage, to_dev(*W), topk_ids, topk_w, expert_offsets, sorted_rows, T, k, y, out,
+                flags, w, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const float* y, const float* topk_w, int64_t T, int32_t k, int32_t D,
+                       const float* residual, float* out, void* stream) {
+  if (T < 0 || k <= 0 || D <= 0) return MOE_E_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!y || !topk_w || !out) return MOE_E_NULLPTR;
+  if (!aligned(y, 4) || !aligned(topk_w, 4) || !aligned(out, 4) ||
+      (residual && !aligned(residual, 4)))
+    return MOE_E_ALIGN;
+  trace("combine", T, D, 0, 0, k, -1);
+  if (launch_combine(y, topk_w, T, k, D, residual, out, (hipStream_t)stream) != hipSuccess)
+    return MOE_E_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_layer(const float* x, const float* gate, const float* bias, const moe_experts* W,
+                     int64_t T, int32_t k, int32_t flags, float* out, int32_t* topk_ids,
+                     float* topk_w, int32_t* expert_offsets, int32_t* sorted_rows, void* ws,
+                     size_t ws_bytes, void* stream) {
+  MOE_TRY(check_experts(W));
+  MOE_TRY(check_gate_up(W));
+  const int D = W->d_model, F = W->d_ff, E = W->num_experts;
+  MOE_TRY(check_dims(T, D, E, k));
+  if (T == 0) return MOE_OK;
+  if (!x || !gate || !out) return MOE_E_NULLPTR;
+  if (!aligned(x, 4) || !aligned(gate, 4) || (bias && !aligned(bias, 4)) || !aligned(out, 4) ||
+      (topk_ids && !aligned(topk_ids, 4)) || (topk_w && !aligned(topk_w, 4)) ||
+      (expert_offsets && !aligned(expert_offsets, 4)) || (sorted_rows && !aligned(sorted_rows, 4)))
+    return MOE_E_ALIGN;
+  const size_t need = moe_workspace_bytes(T, D, F, E, k, W->format, flags);
+  if (!ws || ws_bytes < need) return MOE_E_WORKSPACE;
+  const Workspace w = carve_workspace(ws, T, D, F, E, k, flags);
+  hipStream_t s = (hipStream_t)stream;
+  const ExpertsDev dev = to_dev(*W);
+  int32_t* ids = topk_ids ? topk_ids : w.ids;
+  float* wts = topk_w ? topk_w : w.w;
+  int32_t* offs = expert_offsets ? expert_offsets : w.offsets;
+  int32_t* rows = sorted_rows ? sorted_rows : w.rows;
+  trace("layer generic", T, D, F, E, k, W->format);
+  const float* u = x;
+  if (flags & MOE_F_PRENORM) {
+    HIP_TRY(launch_rmsnorm(x, T, D, PRENORM_EPS, w.xn, s));
+    u = w.xn;
+  }
+  MOE_TRY(do_route(u, T, D, gate, bias, E, k, ids, wts, w, s));
+  HIP_TRY(launch_group(ids, T * k, E, offs, rows, s));
+  return do_ffn(u, MOE_STAGE_FULL, dev, ids, wts, offs, rows, T, k, nullptr, out,
+                flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC), w, s);
+}
+
+moe_status moe_rmsnorm(const float* x, int64_t T, int32_t D, float eps, float* out, void* stream) {
+  if (T < 0 || D <= 0) return MOE_E_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !out) return MOE_E_NULLPTR;
+  if (!aligned(x, 4) || !aligned(out, 4)) return MOE_E_ALIGN;
+  if (!(eps >= 0.0f)) return MOE_E_SHAPE;
+  if (launch_rmsnorm(x, T, D, eps, out, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// LinearGate router: logits = x G + b, top-k with lower-index tie-break,
+// renormalised softmax weights.  (Evidence page, "Layer-qualified experts":
+// learned LinearGate selection; Model card: top-8 of 128 experts.)
+#include <float.h>
+
+#include "internal.hpp"
+
+namespace moe {
+
+// Number of D-slices the router GEMV/GEMM is split into, so that small T still
+// spreads the 1 MiB gate over many CUs.  Each slice is a multiple of 32 rows.
+int router_ksplit(int64_t T, int D) {
+  const int64_t tiles = (T + 7) / 8;
+  int64_t ks = 256 / (tiles > 0 ? tiles : 1);
+  if (ks < 1) ks = 1;
+  if (ks > D / 32) ks = D / 32;
+  int dchunk = (int)(((D + ks - 1) / ks + 31) / 32 * 32);
+  return (D + dchunk - 1) / dchunk;
+}
+
+static int router_dchunk(int D, int ks) { return (int)(((D + ks - 1) / ks + 31) / 32 * 32); }
+
+// part[s][t][e] = sum over the s-th D-slice of x[t][d] * G[d][e].
+// Block: 256 threads = 128 experts x 2 token halves; TT tokens per block.
+template <int TT>
+__global__ __launch_bounds__(256) void router_partial_kernel(const float* __restrict__ x, int64_t T,
+                                                             int D, const float* __restrict__ G,
+                                                             int E, int dchunk,
+                                                             float* __restrict__ part) {
+  constexpr int DC = 32;
+  constexpr int TH = TT / 2;
+  __shared__ float xs[TT][DC];
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * TT;
+  const int s = blockIdx.y;
+  const int d0 = s * dchunk;
+  const int d1 = min(D, d0 + dchunk);
+  const int el = tid & 127, half = tid >> 7;
+  for (int ec = 0; ec < E; ec += 128) {
+    const int e = ec + el;
+    float acc[TH];
+#pragma unroll
+    for (int i = 0; i < TH; ++i) acc[i] = 0.f;
+    for (int dd = d0; dd < d1; dd += DC) {
+      __syncthreads();
+      for (int i = tid; i < TT * DC; i += 256) {
+        const int tt = i / DC, c = i % DC;
+        const int64_t t = t0 + tt;
+        xs[tt][c] = (t < T) ? x[t * D + dd + c] : 0.f;
+      }
+      __syncthreads();
+      if (e < E) {
+#pragma unroll 8
+        for (int c = 0; c < DC; ++c) {
+          const float g = G[(int64_t)(dd + c) * E + e];
+#pragma unroll
+          for (int i = 0; i < TH; ++i) acc[i] = fmaf(xs[half * TH + i][c], g, acc[i]);
+        }
+      }
+    }
+    if (e < E) {
+#pragma unroll
+      for (int i = 0; i < TH; ++i) {
+        const int64_t t = t0 + half * TH + i;
+        if (t < T) part[((int64_t)s * T + t) * E + e] = acc[i];
+      }
+    }
+  }
+}
+
+hipError_t launch_router_partial(const float* x, int64_t T, int D, const float* G, int E,
+                                 float* part, int ksplit, hipStream_t s) {
+  const int dchunk = router_dchunk(D, ksplit);
+  dim3 grid((unsigned)((T + 7) / 8), (unsigned)ksplit);
+  hipLaunchKernelGGL(router_partial_kernel<8>, grid, dim3(256), 0, s, x, T, D, G, E, dchunk, part);
+  return hipGetLastError();
+}
+
+// One wavefront per token: sum the D-slice partials (fixed order), add the
+// bias, pick k winners by (value desc, index asc), then weights
+// w_j = exp(l_j - l_max) / sum_selected exp(l - l_max), written in ascending id order.
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ part, int ksplit,
+                                                   int64_t T, int E,
+                                                   const float* __restrict__ bias, int k,
+                                                   int32_t* __restrict__ ids,
+                                                   float* __restrict__ w) {
+  constexpr int PL = MAX_E / WAVE;  // logits per lane
+  __shared__ float sel_l[4][MAX_K];
+  __shared__ int sel_e[4][MAX_K];
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= T) return;  // whole wavefront leaves together; no block barrier below
+  float v[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int e = i * WAVE + lane;
+    float s = -FLT_MAX;
+    if (e < E) {
+      s = 0.f;
+      for (int p = 0; p < ksplit; ++p) s += part[((int64_t)p * T + t) * E + e];
+      if (bias) s += bias[e];
+    }
+    v[i] = s;
+  }
+  uint32_t taken = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -FLT_MAX;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = i * WAVE + lane;
+      const bool ok = e < E && !((taken >> i) & 1u);
+      if (ok && (v[i] > bv || (v[i] == bv && e < be))) {
+        bv = v[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, WAVE);
+      const int oe = __shfl_xor(be, off, WAVE);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & (WAVE - 1)) == lane) taken |= 1u << (be / WAVE);
+    if (lane == 0) {
+      sel_l[wave][r] = bv;
+      sel_e[wave][r] = be;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  if (lane < k) {
+    const float lmax = sel_l[wave][0];
+    float den = 0.f;
+    for (int r = 0; r < k; ++r) den += expf(sel_l[wave][r] - lmax);
+    const int me = sel_e[wave][lane];
+    int rank = 0;
+    for (int r = 0; r < k; ++r) rank += sel_e[wave][r] < me;
+    ids[t * k + rank] = me;
+    w[t * k + rank] = expf(sel_l[wave][lane] - lmax) / den;
+  }
+}
+
+hipError_t launch_topk(const float* part, int ksplit, int64_t T, int E, const float* bias, int k,
+                       int32_t* ids, float* w, hipStream_t s) {
+  dim3 grid((unsigned)((T + 3) / 4));
+  hipLaunchKernelGGL(topk_kernel, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,94 @@
+"""Seeded workloads shared by the GPU parity tests (inputs only; no layer arithmetic).
+
+Geometry of the toy layer and of the Qwen3-MoE layer (d_model 2048, d_ff 768,
+128 experts, top-8; evidence page, Model card).  Router inputs obey a gap rule
+so the top-k set is unambiguous: the fp64 gap between the k-th and (k+1)-th
+logit is at least 1e-3 (rows failing it are redrawn from their own seed
+stream).  Expert arenas of the large geometry are drawn on the device; the
+oracle reads back the bytes of the experts it needs.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+import moe_synth as S
+from oracle import moe_oracle as O
+
+GAP = 1e-3
+
+
+@dataclasses.dataclass
+class Case:
+    name: str
+    T: int
+    D: int
+    F: int
+    E: int
+    k: int
+    fmt: int
+    x: np.ndarray = None          # [T][D] fp32 (None for the down-only operator)
+    G: np.ndarray = None          # [D][E]
+    b: np.ndarray = None          # [E] or None
+    arena: object = None          # torch uint8 [E][stride] on the device
+    h: np.ndarray = None          # down-only: [T*k][F]
+    ids: np.ndarray = None        # down-only: [T][k] int32
+    w: np.ndarray = None          # down-only: [T][k] fp32
+    redraws: int = 0
+
+    def fetch(self, e: int):
+        blob = self.arena[e].cpu().numpy()
+        return S.split_blob(blob, self.D, self.F, self.fmt)
+
+    def oracle_experts(self):
+        return O.Experts(self.fetch, self.fmt)
+
+
+def gap_rule(G, b, k):
+    def accept(x):
+        return O.topk_gap(O.router_logits(x, G, b), k) >= GAP
+    return accept
+
+
+def router_case(name, cfg, T, D, F, E, k, fmt, zipf: bool, device, host_experts=False,
+                layer=0) -> Case:
+    import torch
+    G = S.gate_matrix(cfg, D, E, layer=layer)
+    b = S.zipf_bias(cfg, E, layer=layer) if zipf else None
+    x = S.hidden(cfg, T, D, layer=layer)
+    red = S.redraw_until(x, cfg, gap_rule(G, b, k), layer=layer) if k < E else np.zeros(T)
+    if host_experts:
+        arena = torch.from_numpy(S.expert_blobs(cfg, E, D, F, fmt, layer=layer)).to(device)
+    else:
+        arena = S.device_arena(cfg, 1, E, D, F, fmt, device)[0]
+    return Case(name, T, D, F, E, k, fmt, x=x, G=G, b=b, arena=arena, redraws=int(red.sum()))
+
+
+def toy(device):
+    """16 tokens x d_model 256, 16 Q8_0 experts (256x128 / 128x256), top-2, no bias."""
+    return router_case("toy", 1, 16, 256, 128, 16, 2, S.FMT_Q8_0, False, device, host_experts=True)
+
+
+def decode(device):
+    """1 token, Qwen geometry, Q8_0, Zipf-biased router."""
+    return router_case("decode", 2, 1, 2048, 768, 128, 8, S.FMT_Q8_0, True, device)
+
+
+def decode_batch(device):
+    """32 tokens, Qwen geometry, 4-bit experts, Zipf-biased router."""
+    return router_case("decode_batch", 3, 32, 2048, 768, 128, 8, S.FMT_Q4, True, device)
+
+
+def prefill_down(device, T=1024):
+    """Down projection only: T tokens routed top-8 over 128 experts, h ~ N(0,1), 4-bit W_down."""
+    cfg, D, F, E, k = 4, 2048, 768, 128, 8
+    G = S.gate_matrix(cfg, D, E)
+    b = S.zipf_bias(cfg, E)
+    xr = S.hidden(cfg, T, D)
+    l = O.router_logits(xr, G, b)
+    ids = O.select_topk(l, k)
+    w = O.routing_weights(l, ids).astype(np.float32)
+    h = S.generator(cfg, 0, S.ROLE_H).standard_normal((T * k, F), dtype=np.float32)
+    arena = S.device_arena(cfg, 1, E, D, F, S.FMT_Q4, device, which=("down",))[0]
+    return Case("prefill_down", T, D, F, E, k, S.FMT_Q4, arena=arena, h=h, ids=ids, w=w)
