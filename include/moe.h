@@ -20,8 +20,11 @@
  *    the host between calls (technical-overview page, "Target boundary").
  *  - Ownership: the caller owns every buffer, including the workspace `ws`
  *    (size from moe_workspace_bytes).  The library allocates no device memory
- *    and keeps no mutable state between calls.  Two calls that share a
- *    workspace must be stream-ordered.
+ *    and keeps no mutable state between calls other than inside `ws`: the
+ *    first 64 KiB of a workspace hold grid-barrier counters of the fused
+ *    kernels, so a workspace must be zero-filled once before its first use
+ *    and must not be shared by calls that may run concurrently (calls that
+ *    share a workspace must be stream-ordered).
  *  - Errors: arguments are validated on the host before anything is enqueued;
  *    on an error the call returns a status != MOE_OK and enqueues nothing.
  *    MOE_E_HIP means a launch failed.  T == 0 is valid and enqueues nothing.

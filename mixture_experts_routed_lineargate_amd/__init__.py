@@ -140,7 +140,8 @@ def workspace(T: int, D: int, F: int, E: int, k: int, fmt: int = FMT_Q8_0, flags
               device="cuda"):
     import torch
     n = moe_workspace_bytes(T, D, F, E, k, fmt, flags)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    # zero-filled: the fused kernels keep grid-barrier counters at its start
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def moe_route(x, gate, bias, k: int, topk_ids, topk_w, ws, stream=None):

@@ -245,6 +245,12 @@ moe_status moe_layer(const float* x, const float* gate, const float* bias, const
   float* wts = topk_w ? topk_w : w.w;
   int32_t* offs = expert_offsets ? expert_offsets : w.offsets;
   int32_t* rows = sorted_rows ? sorted_rows : w.rows;
+  if (decode_fused_supported(dev, T, k, x)) {
+    trace("layer fused decode", T, D, F, E, k, W->format);
+    HIP_TRY(launch_decode_fused(x, gate, bias, dev, out, topk_ids, topk_w, expert_offsets,
+                                sorted_rows, flags, w, s));
+    return MOE_OK;
+  }
   trace("layer generic", T, D, F, E, k, W->format);
   const float* u = x;
   if (flags & MOE_F_PRENORM) {

@@ -8,6 +8,9 @@
 
 namespace moe {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int QK = 32;          // weights per block
 constexpr int WAVE = 64;        // CDNA wavefront
 constexpr int MAX_E = 1024;
@@ -21,10 +24,57 @@ __device__ inline float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, WAVE);
+// Cross-lane reductions on DPP row permutes (a few cycles each) and readlane,
+// instead of ds_bpermute shuffles (an LDS round trip each).  All 64 lanes
+// must be active.
+constexpr int DPP_QUAD_1032 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8 lanes
+constexpr int DPP_ROW_MIRROR = 0x140;      // lane i <-> 15-i within 16 lanes
+
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ inline int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ inline float readlane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+__device__ inline int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// Sum over each group of 8 lanes (every lane of the group gets it).
+__device__ inline float sum8(float v) {
+  v += dpp<DPP_QUAD_1032>(v);
+  v += dpp<DPP_QUAD_2301>(v);
+  v += dpp<DPP_ROW_HALF_MIRROR>(v);
   return v;
+}
+
+// Sum over the wavefront (every lane gets it).
+__device__ inline float wave_sum(float v) {
+  v = sum8(v);
+  v += dpp<DPP_ROW_MIRROR>(v);
+  return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
+
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
+  return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
+}
+
+__device__ inline int wave_min(int v) {
+  v = min(v, dpp<DPP_QUAD_1032>(v));
+  v = min(v, dpp<DPP_QUAD_2301>(v));
+  v = min(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+  v = min(v, dpp<DPP_ROW_MIRROR>(v));
+  return min(min(readlane(v, 0), readlane(v, 16)), min(readlane(v, 32), readlane(v, 48)));
 }
 
 __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -60,7 +110,7 @@ struct Workspace {
 
 int router_ksplit(int64_t T, int D);
 Workspace carve_workspace(void* base, int64_t T, int D, int F, int E, int k, int flags);
-constexpr size_t SYNC_BYTES = 64 * 1024;
+constexpr size_t SYNC_BYTES = 1024 * 1024;  // barrier words and exchange buffers
 
 bool trace_enabled();
 void trace(const char* what, int64_t T, int D, int F, int E, int k, int fmt);
@@ -79,5 +129,12 @@ hipError_t launch_down_generic(const float* h, const ExpertsDev& W, const int32_
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int D,
                           const float* residual, float* out, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, int64_t T, int D, float eps, float* out, hipStream_t s);
+
+// fused single-token decode layer (D 2048, F 768, E 128, k 8)
+bool decode_fused_supported(const ExpertsDev& W, int64_t T, int k, const float* x);
+hipError_t launch_decode_fused(const float* x, const float* gate, const float* bias,
+                               const ExpertsDev& W, float* out, int32_t* ids, float* w,
+                               int32_t* offsets, int32_t* rows, int flags, const Workspace& ws,
+                               hipStream_t s);
 
 }  // namespace moe

@@ -115,15 +115,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
         be = e;
       }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, WAVE);
-      const int oe = __shfl_xor(be, off, WAVE);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    // wave argmax: largest value, then the lowest index among equals
+    const float m = wave_max(bv);
+    be = wave_min(bv == m ? be : 0x7fffffff);
+    bv = m;
     if ((be & (WAVE - 1)) == lane) taken |= 1u << (be / WAVE);
     if (lane == 0) {
       sel_l[wave][r] = bv;

@@ -45,19 +45,24 @@ class Case:
         return O.Experts(self.fetch, self.fmt)
 
 
-def gap_rule(G, b, k):
+def gap_rule(G, b, k, prenorm=False):
+    """Accept rows whose router input (rmsnorm(x) when ``prenorm``) has an fp64
+    k-th/(k+1)-th logit gap of at least GAP."""
     def accept(x):
-        return O.topk_gap(O.router_logits(x, G, b), k) >= GAP
+        u = O.rmsnorm(x) if prenorm else x
+        return O.topk_gap(O.router_logits(u, G, b), k) >= GAP
     return accept
 
 
 def router_case(name, cfg, T, D, F, E, k, fmt, zipf: bool, device, host_experts=False,
-                layer=0) -> Case:
+                layer=0, prenorm=False) -> Case:
     import torch
     G = S.gate_matrix(cfg, D, E, layer=layer)
     b = S.zipf_bias(cfg, E, layer=layer) if zipf else None
     x = S.hidden(cfg, T, D, layer=layer)
-    red = S.redraw_until(x, cfg, gap_rule(G, b, k), layer=layer) if k < E else np.zeros(T)
+    if prenorm:
+        x *= np.float32(2.5)                      # exercise the normalisation
+    red = S.redraw_until(x, cfg, gap_rule(G, b, k, prenorm), layer=layer) if k < E else np.zeros(T)
     if host_experts:
         arena = torch.from_numpy(S.expert_blobs(cfg, E, D, F, fmt, layer=layer)).to(device)
     else:

@@ -164,14 +164,45 @@ def test_edge_shapes(T, D, F, E, k, fmt):
     check_out(g["out"], r["out"])
 
 
-def test_prenorm_flag(toy_case):
-    c = toy_case
-    x3 = (c.x * 3.0).astype(np.float32)         # rmsnorm(3x) has the same routing as x
-    g = run_layer(c, M.F_RESIDUAL | M.F_PRENORM, x=x3)
-    u = O.rmsnorm(x3)
-    r = O.moe_layer(u, c.G, c.b, c.oracle_experts(), c.k, residual=True)
+def test_prenorm_flag():
+    c = cases.router_case("toy_prenorm", 7, 16, 256, 128, 16, 2, S.FMT_Q8_0, False, DEV,
+                          host_experts=True, prenorm=True)
+    g = run_layer(c, M.F_RESIDUAL | M.F_PRENORM)
+    r = O.moe_layer(O.rmsnorm(c.x), c.G, c.b, c.oracle_experts(), c.k, residual=True)
     check_routing(g, r)
     check_out(g["out"], r["out"])
+
+
+@pytest.mark.parametrize("fmt", [S.FMT_Q8_0, S.FMT_Q4])
+@pytest.mark.parametrize("flags", [0, M.F_RESIDUAL, M.F_RESIDUAL | M.F_PRENORM])
+def test_single_token_layer(fmt, flags):
+    """Single-token Qwen-geometry layer (the fused one-launch decode path), both formats."""
+    pre = bool(flags & M.F_PRENORM)
+    c = cases.router_case(f"decode{fmt}", 20 + fmt, 1, 2048, 768, 128, 8, fmt, True, DEV,
+                          prenorm=pre)
+    g = run_layer(c, flags)
+    u = O.rmsnorm(c.x) if pre else c.x
+    r = O.moe_layer(u, c.G, c.b, c.oracle_experts(), c.k, residual=bool(flags & M.F_RESIDUAL))
+    check_routing(g, r)
+    check_out(g["out"], r["out"])
+
+
+def test_single_token_repeated_calls(decode_case):
+    """Many consecutive one-launch decode calls on one workspace (its barrier counter keeps
+    running across calls): every call matches the oracle and no wait timed out."""
+    c = decode_case
+    ws = M.workspace(1, c.D, c.F, c.E, c.k, c.fmt, M.F_RESIDUAL)
+    G, b, ex = dev(c.G), dev(c.b), experts_of(c)
+    experts = c.oracle_experts()
+    out = torch.empty((1, c.D), dtype=torch.float32, device=DEV)
+    for rep in range(6):
+        x = S.hidden(400 + rep, 1, c.D)
+        S.redraw_until(x, 400 + rep, cases.gap_rule(c.G, c.b, c.k))
+        M.moe_layer(dev(x), G, b, ex, c.k, out, flags=M.F_RESIDUAL, ws=ws)
+        torch.cuda.synchronize()
+        r = O.moe_layer(x, c.G, c.b, experts, c.k, residual=True)
+        check_out(out.cpu().numpy(), r["out"], f"call {rep}")
+    assert int(ws[64:68].view(torch.int32).item()) == 0, "grid barrier timed out"
 
 
 def test_empty_input(toy_case):
