@@ -79,7 +79,10 @@ enum {
 enum {
   MOE_F_RESIDUAL = 1,      /* out += layer input                                       */
   MOE_F_DETERMINISTIC = 2, /* fp outputs bit-reproducible run to run                   */
-  MOE_F_PRENORM = 4        /* moe_layer only: the layer input is rmsnorm(x, eps=1e-6)   */
+  MOE_F_PRENORM = 4,       /* moe_layer only: the layer input is rmsnorm(x, eps=1e-6)   */
+  MOE_F_FP16_ACT = 8       /* MFMA expert kernels: round activations to fp16 once       */
+                           /* instead of carrying them as two fp16 terms (hi + lo); half */
+                           /* the matrix work, ~1e-3 RMS-relative output error           */
 };
 
 /* One layer's experts (host struct holding device pointers).  Expert e's gate
@@ -130,6 +133,15 @@ moe_status moe_group(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
                      void* stream);
 
 /* Routed expert SwiGLU FFNs.
+ * Precision: products of exactly decoded weights and activations accumulate in
+ * fp32.  When D and F are multiples of 128 (and weight bases / strides are
+ * 8-byte aligned, fp32 buffers 16-byte aligned) the grouped MFMA kernels run:
+ * activations enter the matrix cores as two fp16 terms (hi + lo, about fp32
+ * accuracy), or as one fp16 rounding with MOE_F_FP16_ACT; |activations| must
+ * stay below 65504.  Other shapes take generic fp32 kernels.
+ * Combine: without MOE_F_DETERMINISTIC the weighted sum into `out` uses fp32
+ * atomics (summation order varies run to run); with it, y is materialised and
+ * summed in j order.
  *   stage MOE_STAGE_FULL: in = x [T][D]; for row r = t*k + j with e = ids[t][j]:
  *     h = silu(x_t W_gate_e) * (x_t W_up_e), y_r = h W_down_e.
  *   stage MOE_STAGE_DOWN: in = h [T*k][F]; y_r = h_r W_down_e (the routed

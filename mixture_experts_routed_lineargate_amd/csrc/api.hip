@@ -102,9 +102,35 @@ static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const 
                          const float* w, const int32_t* offsets, const int32_t* rows, int64_t T,
                          int k, float* y, float* out, int flags, const Workspace& ws,
                          hipStream_t s) {
-  (void)offsets;
-  (void)rows;
-  const char* path = stage == MOE_STAGE_FULL ? "ffn generic gate/up+down" : "ffn generic down";
+  const bool full = stage == MOE_STAGE_FULL;
+  const int64_t R = T * k;
+  auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
+  if (grouped_supported(W, full) && a16(in) && a16(y) && a16(out)) {
+    const bool split = !(flags & MOE_F_FP16_ACT);
+    trace(full ? (split ? "ffn grouped mfma gate/up+down (split fp16)"
+                        : "ffn grouped mfma gate/up+down (fp16)")
+               : (split ? "ffn grouped mfma down (split fp16)" : "ffn grouped mfma down (fp16)"),
+          T, W.D, W.F, W.E, k, W.fmt);
+    const float* h = in;
+    int a_mode = GG_A_FLAT;
+    if (full) {
+      HIP_TRY(launch_grouped_gateup(in, GG_A_TOKEN, W, offsets, rows, R, k, ws.h, split, s));
+      h = ws.h;
+      a_mode = GG_A_SORTED;
+    }
+    const float* res = (full && (flags & MOE_F_RESIDUAL)) ? in : nullptr;
+    if (out && !y && !(flags & MOE_F_DETERMINISTIC)) {
+      // combine fused into the down epilogue: out starts at the residual (or 0)
+      HIP_TRY(launch_init_out(out, res, T * (int64_t)W.D, s));
+      HIP_TRY(launch_grouped_down(h, a_mode, W, offsets, rows, w, R, k, out, nullptr, split, s));
+      return MOE_OK;
+    }
+    float* ybuf = y ? y : ws.y;
+    HIP_TRY(launch_grouped_down(h, a_mode, W, offsets, rows, nullptr, R, k, nullptr, ybuf, split, s));
+    if (out) HIP_TRY(launch_combine(ybuf, w, T, k, W.D, res, out, s));
+    return MOE_OK;
+  }
+  const char* path = full ? "ffn generic gate/up+down" : "ffn generic down";
   trace(path, T, W.D, W.F, W.E, k, W.fmt);
   const float* h = in;
   if (stage == MOE_STAGE_FULL) {
@@ -260,7 +286,7 @@ moe_status moe_layer(const float* x, const float* gate, const float* bias, const
   MOE_TRY(do_route(u, T, D, gate, bias, E, k, ids, wts, w, s));
   HIP_TRY(launch_group(ids, T * k, E, offs, rows, s));
   return do_ffn(u, MOE_STAGE_FULL, dev, ids, wts, offs, rows, T, k, nullptr, out,
-                flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC), w, s);
+                flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC | MOE_F_FP16_ACT), w, s);
 }
 
 moe_status moe_rmsnorm(const float* x, int64_t T, int32_t D, float eps, float* out, void* stream) {

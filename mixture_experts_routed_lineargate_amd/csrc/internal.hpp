@@ -130,6 +130,19 @@ hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int 
                           const float* residual, float* out, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, int64_t T, int D, float eps, float* out, hipStream_t s);
 
+// grouped GEMM on MFMA (batched / prefill expert FFN)
+enum { GG_A_TOKEN = 0, GG_A_FLAT = 1, GG_A_SORTED = 2 };   // activation row of sorted row i:
+                                                          // x[rows[i]/k], h[rows[i]], h[i]
+enum { GG_OUT_H = 0, GG_OUT_ATOMIC = 1, GG_OUT_Y = 2 };
+bool grouped_supported(const ExpertsDev& W, bool need_gate_up);
+hipError_t launch_grouped_gateup(const float* a, int a_mode, const ExpertsDev& W,
+                                 const int32_t* offsets, const int32_t* rows, int64_t R, int k,
+                                 float* h_sorted, bool split, hipStream_t s);
+hipError_t launch_grouped_down(const float* a, int a_mode, const ExpertsDev& W,
+                               const int32_t* offsets, const int32_t* rows, const float* topk_w,
+                               int64_t R, int k, float* out, float* y, bool split, hipStream_t s);
+hipError_t launch_init_out(float* out, const float* residual, int64_t n, hipStream_t s);
+
 // fused single-token decode layer (D 2048, F 768, E 128, k 8)
 bool decode_fused_supported(const ExpertsDev& W, int64_t T, int k, const float* x);
 hipError_t launch_decode_fused(const float* x, const float* gate, const float* bias,

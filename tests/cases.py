@@ -36,6 +36,7 @@ class Case:
     ids: np.ndarray = None        # down-only: [T][k] int32
     w: np.ndarray = None          # down-only: [T][k] fp32
     redraws: int = 0
+    ref: object = None            # cached oracle result, when a test stores one
 
     def fetch(self, e: int):
         blob = self.arena[e].cpu().numpy()
@@ -97,3 +98,24 @@ def prefill_down(device, T=1024):
     h = S.generator(cfg, 0, S.ROLE_H).standard_normal((T * k, F), dtype=np.float32)
     arena = S.device_arena(cfg, 1, E, D, F, S.FMT_Q4, device, which=("down",))[0]
     return Case("prefill_down", T, D, F, E, k, S.FMT_Q4, arena=arena, h=h, ids=ids, w=w)
+
+
+def stack_layers(cfg, L, E, D, k):
+    """Per-layer LinearGate matrices and Zipf biases of a layer stack (independent seeds)."""
+    return [(S.gate_matrix(cfg, D, E, layer=l), S.zipf_bias(cfg, E, layer=l)) for l in range(L)]
+
+
+def stack_oracle(x_rows, gates, arena, D, F, k, fmt):
+    """Oracle trajectory of a few token rows through every layer of the stack.
+
+    Tokens are independent (no attention), so the trajectory of a token does not
+    depend on which other tokens share its microbatch.  Returns the per-layer
+    oracle results (``out`` = o_l, ``logits``, ``ids``)."""
+    def layers():
+        for l, (G, b) in enumerate(gates):
+            fetch = (lambda e, l=l: S.split_blob(arena[l, e].cpu().numpy(), D, F, fmt))
+            yield G, b, O.Experts(fetch, fmt)
+    def progress(l, r):
+        if l % 8 == 7:
+            print(f"  oracle: layer {l + 1}/{len(gates)} done", flush=True)
+    return O.stack(x_rows, layers(), k, on_layer=progress)

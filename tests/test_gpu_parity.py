@@ -114,8 +114,17 @@ def test_separate_calls_parity(name, request):
     check_out(out2.cpu().numpy(), r["out"], "fused out")
 
 
-def test_prefill_down_parity():
+@pytest.fixture(scope="module")
+def down_case():
     c = cases.prefill_down(DEV)
+    c.ref = O.down_combine(c.h, c.ids, c.w, c.oracle_experts())
+    return c
+
+
+@pytest.mark.parametrize("flags", [0, M.F_FP16_ACT, M.F_DETERMINISTIC])
+def test_prefill_down_parity(down_case, flags):
+    """1024 tokens x top-8 routed rows through the 4-bit down projection plus combine."""
+    c = down_case
     T, k = c.T, c.k
     ids, w = dev(c.ids), dev(c.w)
     offs = torch.empty(c.E + 1, dtype=torch.int32, device=DEV)
@@ -123,13 +132,13 @@ def test_prefill_down_parity():
     out = torch.empty((T, c.D), dtype=torch.float32, device=DEV)
     ws = M.workspace(T, c.D, c.F, c.E, k, c.fmt)
     M.moe_group(ids, c.E, offs, rows, ws)
-    M.moe_expert_ffn(dev(c.h), M.STAGE_DOWN, experts_of(c), ids, w, offs, rows, out=out, ws=ws)
+    M.moe_expert_ffn(dev(c.h), M.STAGE_DOWN, experts_of(c), ids, w, offs, rows, out=out,
+                     flags=flags, ws=ws)
     torch.cuda.synchronize()
     roff, rrows = O.group(c.ids, c.E)
     assert np.array_equal(offs.cpu().numpy(), roff)
     assert np.array_equal(rows.cpu().numpy(), rrows)
-    ref = O.down_combine(c.h, c.ids, c.w, c.oracle_experts())
-    check_out(out.cpu().numpy(), ref)
+    check_out(out.cpu().numpy(), c.ref)
 
 
 def test_prefill_layer_sampled_tokens():
