@@ -1,17 +1,31 @@
 #!/usr/bin/env python3
 """Throughput of the routed MoE layer on one MI355X.
 
-Default workload: single-token decode through Qwen3-MoE-geometry MoE layers
-(d_model 2048, d_ff 768, 128 Q8_0 experts, Zipf-biased LinearGate, top-8).
-One step = one token through 48 distinct layers chained with residual +
-RMSNorm (48 moe_layer calls, captured once as a HIP graph and replayed), so
-consecutive layer calls never reuse expert weights and the 256 MB Infinity
-Cache cannot serve them.  ``value`` = routed MoE-layer tokens/s = 48 * steps /
-elapsed.
+Headline workload (the JSON line's ``value``): single-token decode through
+Qwen3-MoE-geometry MoE layers (d_model 2048, d_ff 768, 128 Q8_0 experts,
+Zipf-biased LinearGate, top-8).  One step = one token through 48 distinct layers
+chained with residual + RMSNorm (48 moe_layer calls, captured once as a HIP
+graph and replayed), so consecutive layer calls never reuse expert weights and
+the 256 MB Infinity Cache cannot serve them.  ``value`` = routed MoE-layer
+tokens/s = 48 * steps / elapsed.
 
-Prints ONE JSON line.  ``roofline`` reports the dominant kernel (the fused
-decode layer) against the 8 TB/s HBM peak; ``cpu_baseline`` times the fp64
-CPU oracle on a bounded sample of the same workload.
+The same run also measures, under ``workloads``:
+  decode_batch   32 tokens x 16 chained 4-bit layers (residual + RMSNorm)
+  prefill_down   the down projection + combine operator: 1024 tokens routed
+                 top-8 (8192 rows of 768 fp32 activations), 4-bit W_down,
+                 rotating over 16 layers' routers and weights; both the
+                 two-term (hi+lo fp16) and the single-fp16 activation variants
+  prefill_stack  2048 tokens as two 1024-token microbatches through 48 Q8_0
+                 layers (residual + RMSNorm), 96 layer calls per pass
+Each reports its time per call, algorithmic GB/s against the 8 TB/s HBM peak
+and algorithmic MFMA TFLOP/s against the 2.5 PFLOP/s dense fp16 peak (the
+matrix cores see fp16 operands; flops are counted once, without the second
+activation term).  Algorithmic bytes = expert weights of the U experts that
+received rows + router matrix + activations in + outputs out.
+
+Prints ONE JSON line.  ``roofline`` reports the dominant kernel of the headline
+workload (the fused decode layer); ``cpu_baseline`` times the fp64 CPU oracle on
+a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -26,11 +40,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2516.6          # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 D, F, E, K = 2048, 768, 128, 8
 Q8_BLOB = 5_013_504                      # one Q8_0 expert: 3 * 2048 * 768 / 32 * 34 bytes
-DECODE_ALGO_BYTES = K * Q8_BLOB + D * E * 4 + E * 4 + 2 * D * 4   # = 41,173,504
+Q4_BLOB = 2_654_208                      # one 4-bit expert: 3 * 2048 * 768 / 32 * 18 bytes
+Q4_DOWN = 884_736                        # one 4-bit W_down: 2048 * 768 / 32 * 18 bytes
+GATE_BYTES = D * E * 4 + E * 4           # router matrix + bias
+DECODE_ALGO_BYTES = K * Q8_BLOB + GATE_BYTES + 2 * D * 4   # = 41,173,504
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "mixture_experts_routed_lineargate_amd", "csrc", "decode.hip")
+WORKLOADS = ("decode_batch", "prefill_down", "prefill_stack")
 
 
 def parse():
@@ -41,6 +60,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--workloads", default=",".join(WORKLOADS),
+                    help="comma list of extra workloads to measure (empty for none)")
     return ap.parse_args()
 
 
@@ -68,7 +89,6 @@ def cpu_baseline(arena, layers_np, budget_s: float):
     copied to the host; the timed call is the whole oracle layer (routing,
     dequantising the 8 experts, SwiGLU FFNs, combine).
     """
-    import numpy as np
     import moe_synth as S
     from oracle import moe_oracle as O
     try:
@@ -93,13 +113,159 @@ def cpu_baseline(arena, layers_np, budget_s: float):
                       f"routing, dequantising the 8 selected experts, SwiGLU, combine); {total:.1f} s"}
 
 
+def graph_time_ms(torch, fn, stream, warmup: int, iters: int) -> float:
+    """Capture fn() once as a HIP graph; return the mean ms per replay (events on `stream`)."""
+    with torch.cuda.stream(stream):
+        fn()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fn()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(iters):
+            graph.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def n_active(torch, ids) -> int:
+    return int(torch.unique(ids).numel())
+
+
+def rates(ms: float, nbytes: float, flops: float) -> dict:
+    s = ms / 1e3
+    gbps = nbytes / s / 1e9
+    tf = flops / s / 1e12
+    return {"ms_per_call": round(ms, 5), "algorithmic_bytes": int(nbytes),
+            "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "mfma_tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_FP16_PEAK_TFLOPS, 4)}
+
+
+def ffn_flops(rows: int) -> float:
+    return 2.0 * rows * D * F * 3
+
+
+def bench_decode_batch(torch, M, S, dev, stream, iters):
+    """32 tokens through 16 chained 4-bit layers (residual + RMSNorm), one graph per pass."""
+    T, L4 = 32, 16
+    arena = S.device_arena(3, L4, E, D, F, S.FMT_Q4, dev)
+    gates = [(torch.from_numpy(S.gate_matrix(3, D, E, layer=l)).to(dev),
+              torch.from_numpy(S.zipf_bias(3, E, layer=l)).to(dev)) for l in range(L4)]
+    ex = [M.Experts.from_blobs(arena[l], D, F, S.FMT_Q4) for l in range(L4)]
+    flags = M.F_RESIDUAL | M.F_PRENORM
+    ws = M.workspace(T, D, F, E, K, S.FMT_Q4, flags)
+    bufs = [torch.from_numpy(S.hidden(3, T, D)).to(dev)] + \
+           [torch.empty((T, D), dtype=torch.float32, device=dev) for _ in range(L4)]
+    ids = torch.empty((L4, T, K), dtype=torch.int32, device=dev)
+
+    def one():
+        for l in range(L4):
+            M.moe_layer(bufs[l], gates[l][0], gates[l][1], ex[l], K, bufs[l + 1],
+                        flags=flags if l > 0 else M.F_RESIDUAL, topk_ids=ids[l], ws=ws,
+                        stream=stream)
+    ms = graph_time_ms(torch, one, stream, 3, iters) / L4
+    U = sum(n_active(torch, ids[l]) for l in range(L4)) / L4
+    nbytes = U * Q4_BLOB + GATE_BYTES + 2 * T * D * 4
+    flops = ffn_flops(T * K) + 2.0 * T * D * E
+    r = {"workload": "decode batch: 32 tokens x Qwen3-MoE layer, 4-bit experts, Zipf router, top-8; "
+                     "16 distinct layers chained (residual + RMSNorm)",
+         "tokens_per_s": round(T / (ms / 1e3), 1), "mean_active_experts": round(U, 2)}
+    r.update(rates(ms, nbytes, flops))
+    del arena
+    return r, ws
+
+
+def bench_prefill_down(torch, M, S, dev, stream, iters):
+    """Down projection + combine over 8192 routed rows, rotating over 16 layers."""
+    T, L4 = 1024, 16
+    R = T * K
+    arena = S.device_arena(4, L4, E, D, F, S.FMT_Q4, dev, which=("down",))
+    ex = [M.Experts.from_blobs(arena[l], D, F, S.FMT_Q4) for l in range(L4)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    h = torch.randn((R, F), generator=g, device=dev, dtype=torch.float32)
+    xr = torch.randn((T, D), generator=g, device=dev, dtype=torch.float32)
+    ws = M.workspace(T, D, F, E, K, S.FMT_Q4)
+    ids = torch.empty((L4, T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((L4, T, K), dtype=torch.float32, device=dev)
+    offs = torch.empty((L4, E + 1), dtype=torch.int32, device=dev)
+    rows = torch.empty((L4, R), dtype=torch.int32, device=dev)
+    for l in range(L4):       # routing by this library's router (setup, untimed)
+        G = torch.from_numpy(S.gate_matrix(4, D, E, layer=l)).to(dev)
+        b = torch.from_numpy(S.zipf_bias(4, E, layer=l)).to(dev)
+        M.moe_route(xr, G, b, K, ids[l], w[l], ws)
+        M.moe_group(ids[l], E, offs[l], rows[l], ws)
+    torch.cuda.synchronize()
+    out = torch.empty((T, D), dtype=torch.float32, device=dev)
+    U = sum(n_active(torch, ids[l]) for l in range(L4)) / L4
+    nbytes = U * Q4_DOWN + R * F * 4 + T * D * 4 + R * 4 * 3 + (E + 1) * 4
+    flops = 2.0 * R * F * D
+    res = {"workload": "prefill down projection + combine: 1024 tokens routed top-8 of 128 "
+                       "(8192 rows x 768 fp32), 4-bit W_down 768x2048, Zipf routers; "
+                       "rotating over 16 layers",
+           "mean_active_experts": round(U, 2)}
+    for name, fl in (("split_fp16", 0), ("fp16", M.F_FP16_ACT)):
+        def one(fl=fl):
+            for l in range(L4):
+                M.moe_expert_ffn(h, M.STAGE_DOWN, ex[l], ids[l], w[l], offs[l], rows[l],
+                                 out=out, flags=fl, ws=ws, stream=stream)
+        ms = graph_time_ms(torch, one, stream, 3, iters) / L4
+        r = {"tokens_per_s": round(T / (ms / 1e3), 1)}
+        r.update(rates(ms, nbytes, flops))
+        res[name] = r
+    del arena
+    return res
+
+
+def bench_prefill_stack(torch, M, S, dev, stream, arena, gates, iters):
+    """2048 tokens as 2 x 1024 through 48 Q8_0 layers (residual + RMSNorm)."""
+    T, MB = 2048, 1024
+    L = arena.shape[0]
+    ex = [M.Experts.from_blobs(arena[l], D, F, S.FMT_Q8_0) for l in range(L)]
+    flags = M.F_RESIDUAL | M.F_PRENORM
+    ws = M.workspace(MB, D, F, E, K, S.FMT_Q8_0, flags)
+    x0 = torch.from_numpy(S.hidden(5, T, D)).to(dev)
+    outs = torch.empty((L, T, D), dtype=torch.float32, device=dev)
+    ids = torch.empty((L, T, K), dtype=torch.int32, device=dev)
+
+    def one():
+        for mb in range(T // MB):
+            sl = slice(mb * MB, (mb + 1) * MB)
+            for l in range(L):
+                src = x0[sl] if l == 0 else outs[l - 1, sl]
+                M.moe_layer(src, gates[l][0], gates[l][1], ex[l], K, outs[l, sl],
+                            flags=flags if l > 0 else M.F_RESIDUAL, topk_ids=ids[l, sl], ws=ws,
+                            stream=stream)
+    ms = graph_time_ms(torch, one, stream, 2, iters)
+    if not torch.isfinite(outs[L - 1]).all():
+        raise RuntimeError("prefill stack: non-finite output")
+    Us = [n_active(torch, ids[l, mb * MB:(mb + 1) * MB]) for mb in range(T // MB) for l in range(L)]
+    nbytes = sum(Us) * Q8_BLOB + len(Us) * (GATE_BYTES + 2 * MB * D * 4)
+    flops = len(Us) * (ffn_flops(MB * K) + 2.0 * MB * D * E)
+    r = {"workload": "prefill: 2048 tokens as two 1024-token microbatches through 48 Qwen3-MoE "
+                     "layers (128 Q8_0 experts each, Zipf routers, top-8, residual + RMSNorm)",
+         "tokens_per_s": round(T / (ms / 1e3), 1),
+         "token_layers_per_s": round(T * L / (ms / 1e3), 1),
+         "mean_active_experts": round(sum(Us) / len(Us), 2)}
+    r.update(rates(ms, nbytes, flops))
+    r["ms_per_call"] = round(ms / len(Us), 5)
+    r["ms_per_pass"] = round(ms, 4)
+    del outs
+    return r
+
+
 def main():
     a = parse()
     if a.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; runs on more than one GPU are "
                                    "not part of it (the sharding plan is documented, not run)"}))
         sys.exit(2)
-    import numpy as np
     import torch
 
     import moe_synth as S
@@ -122,33 +288,17 @@ def main():
             M.moe_layer(bufs[l], gates[l][0], gates[l][1], experts[l], K, bufs[l + 1],
                         flags=flags if l > 0 else M.F_RESIDUAL, ws=ws, stream=stream)
 
-    with torch.cuda.stream(stream):
-        one_pass()
-    stream.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        one_pass()
-    for _ in range(a.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        for _ in range(a.steps):
-            graph.replay()
-        end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    err = int(ws[64:68].view(torch.int32).item())    # grid-barrier timeout flag
+    ms_step = graph_time_ms(torch, one_pass, stream, a.warmup, a.steps)
+    err = int(ws[64:68].view(torch.int32).item())    # exchange-wait timeout flag
     if err:
-        raise RuntimeError("decode kernel reported a grid-barrier timeout")
+        raise RuntimeError("decode kernel reported an exchange-wait timeout")
     if not torch.isfinite(bufs[L]).all():
         raise RuntimeError("non-finite output")
+    print(f"[bench] decode: {ms_step * 1e3 / L:.2f} us per layer call", file=sys.stderr, flush=True)
 
-    ms_step = ms / a.steps
-    launch_s = ms / 1e3 / (a.steps * L)              # average fused-layer launch, events on its stream
+    launch_s = ms_step / 1e3 / L                    # average fused-layer launch, events on its stream
     achieved = DECODE_ALGO_BYTES / launch_s / 1e9
-    value = a.steps * L / (ms / 1e3)
+    value = L / (ms_step / 1e3)
     line = {
         "metric": "routed MoE-layer tokens/s",
         "value": round(value, 1),
@@ -178,6 +328,25 @@ def main():
             "avg_launch_us": round(launch_s * 1e6, 3),
         },
     }
+    want = [w for w in a.workloads.split(",") if w]
+    extra = {}
+    iters = max(3, min(20, a.steps // 10))
+    if "decode_batch" in want:
+        extra["decode_batch"], _ = bench_decode_batch(torch, M, S, dev, stream, iters)
+        print(f"[bench] decode_batch: {extra['decode_batch']['ms_per_call'] * 1e3:.2f} us per layer",
+              file=sys.stderr, flush=True)
+    if "prefill_down" in want:
+        extra["prefill_down"] = bench_prefill_down(torch, M, S, dev, stream, iters)
+        print(f"[bench] prefill_down: {extra['prefill_down']['split_fp16']['ms_per_call'] * 1e3:.2f} "
+              f"/ {extra['prefill_down']['fp16']['ms_per_call'] * 1e3:.2f} us per call",
+              file=sys.stderr, flush=True)
+    if "prefill_stack" in want:
+        extra["prefill_stack"] = bench_prefill_stack(torch, M, S, dev, stream, arena, gates,
+                                                     max(2, iters // 4))
+        print(f"[bench] prefill_stack: {extra['prefill_stack']['ms_per_pass']:.3f} ms per pass",
+              file=sys.stderr, flush=True)
+    if extra:
+        line["workloads"] = extra
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(arena, layers_np, a.cpu_seconds)
     print(json.dumps(line), flush=True)
