@@ -40,9 +40,9 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NT = 256;               // threads per workgroup
-constexpr int NW = NT / WAVE;         // 4 wavefronts
-constexpr int BN = 128;               // weight rows per tile
+constexpr int NT = 512;               // threads per workgroup (8 wavefronts, one workgroup per CU)
+constexpr int NW = NT / WAVE;
+constexpr int BN = 256;               // weight rows per tile (32 per wavefront)
 constexpr int BKB = 4;                // blocks per K chunk
 constexpr int BK = BKB * QK;          // 128 values per K chunk
 constexpr int AS = BK + 8;            // fp16 per LDS activation row (272 B: conflict-free b128 reads)
@@ -74,8 +74,8 @@ struct Fmt {
   static constexpr int BB = FMT == MOE_FMT_Q8_0 ? 34 : 18;
   static constexpr int CB = BKB * BB;          // bytes of one row in one K chunk (136 / 72)
   static constexpr int U8 = CB / 8;            // 8-byte units per row chunk (17 / 9)
-  static constexpr int BUNITS = BN * U8;
-  static constexpr int BITERS = (BUNITS + NT - 1) / NT;
+  static constexpr int HUNITS = BN / 2 * U8;   // 8-byte units of half a tile's rows
+  static constexpr int HITERS = (HUNITS + NT - 1) / NT;
   static_assert(CB % 8 == 0, "row chunks are 8-byte multiples");
 };
 
@@ -84,12 +84,6 @@ __device__ inline int xcd_swizzle(int bid, int total) {
   const int x = bid & 7, s = bid >> 3;
   const int q = total >> 3, r = total & 7;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + s;
-}
-
-// Rows of expert e, clamped so that bad offsets cannot index outside [0, R).
-__device__ inline int group_count(const Args& p, int e) {
-  const int b = max(0, p.offsets[e]), en = min(p.R, p.offsets[e + 1]);
-  return max(0, en - b);
 }
 
 __device__ inline uint32_t lds32(const uint8_t* p, int off) { return *(const uint32_t*)(p + off); }
@@ -155,31 +149,51 @@ __device__ inline h8 block_frag(const uint8_t* row, int b, int g) {
   return r.v;
 }
 
+constexpr int TW = 8;                  // tiles per metadata window
+
+// Persistent: each workgroup walks tiles L = slot, slot + G, ... where slot()
+// gives the workgroups of one XCD consecutive tiles (tiles are numbered M-tile
+// major, so an XCD works on a few M-tiles x all their N-tiles at a time and
+// shares activation rows and weight tiles in its L2).
+//
+// Row metadata (activation row, token, combine weight) of a window of TW tiles
+// is fetched into LDS in one batch, so the dependent index loads cost one round
+// trip per window rather than per tile.  Every load of the K loop is
+// unconditional (padding rows read a valid row and are never stored), so the
+// compiler's wait counts stay exact and the two-chunk prefetch is not drained.
+//
+// K pipeline: two register stages and two LDS buffers.  Chunk c+2 is fetched
+// while chunk c is multiplied; one barrier per chunk.
 template <int FMT, int STAGE, int MSUB, bool SPLIT>
-__global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(Args p) {
+__global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Args p) {
   using FF = Fmt<FMT>;
   constexpr int BM = 16 * MSUB;
   constexpr int BS = FF::CB;                        // LDS bytes per weight row
-  __shared__ __attribute__((aligned(16))) _Float16 a_hi[BM * AS];
-  __shared__ __attribute__((aligned(16))) _Float16 a_lo[SPLIT ? BM * AS : 8];
-  __shared__ __attribute__((aligned(16))) uint8_t bw[BN * BS + 16];   // +16: aligned reads may pass the end
-  __shared__ int tstart[MAX_E + 1];
-  __shared__ int arow[BM];
-  __shared__ int flat[BM];
-  __shared__ int tile_info[4];
+  constexpr int A_ELEMS = BM * AS;
+  constexpr int B_BYTES = BN * BS + 16;             // +16: aligned reads may pass the end
+  static_assert(TW * BM <= NT, "one metadata entry per thread");
+  __shared__ __attribute__((aligned(16))) _Float16 a_hi[2][A_ELEMS];
+  __shared__ __attribute__((aligned(16))) _Float16 a_lo[2][SPLIT ? A_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint8_t bw[2][B_BYTES];
+  __shared__ int offs[MAX_E + 1];                   // expert_offsets clamped to [0, R]
+  __shared__ int tstart[MAX_E + 1];                 // M-tiles of experts < e
+  __shared__ int total_m;
+  __shared__ int m_src[TW][BM];                     // activation row (always a valid row)
+  __shared__ int m_flat[TW][BM];                    // flat row t*k+j, -1 = padding
+  __shared__ int m_tok[TW][BM];                     // token of the row
+  __shared__ float m_w[TW][BM];                     // combine weight of the row
 
   const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
   const int E = p.E;
-
-  // ---- tile map: scan of ceil(count_e / BM) over experts (wavefront 0) ----
+  for (int e = tid; e <= E; e += NT) offs[e] = min(max(p.offsets[e], 0), p.R);
+  __syncthreads();
   if (wave == 0) {
     const int per = (E + WAVE - 1) / WAVE;
     const int e0 = lane * per;
+    auto tiles_of = [&](int e) { return (max(offs[e + 1] - offs[e], 0) + BM - 1) / BM; };
     int loc = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < E) loc += (group_count(p, e) + BM - 1) / BM;
-    }
+    for (int i = 0; i < per; ++i)
+      if (e0 + i < E) loc += tiles_of(e0 + i);
     int inc = loc;
 #pragma unroll
     for (int o = 1; o < WAVE; o <<= 1) {
@@ -187,117 +201,48 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(Args p) {
       if (lane >= o) inc += v;
     }
     int run = inc - loc;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < E) {
-        tstart[e] = run;
-        run += (group_count(p, e) + BM - 1) / BM;
+    for (int i = 0; i < per; ++i)
+      if (e0 + i < E) {
+        tstart[e0 + i] = run;
+        run += tiles_of(e0 + i);
       }
-    }
-    if (lane == WAVE - 1) tile_info[0] = inc;
+    if (lane == WAVE - 1) total_m = inc;
   }
   __syncthreads();
-  const int total_m = tile_info[0];
   const int total = total_m * p.n_tiles;
-  if ((int)blockIdx.x >= total) return;              // uniform over the workgroup
-  const int L = xcd_swizzle(blockIdx.x, total);
-  const int mg = L / p.n_tiles, nt = L % p.n_tiles;
-  // expert = last e with tstart[e] <= mg (empty experts share the next start)
-  int lo_e = 0, hi_e = E - 1;
-  while (lo_e < hi_e) {
-    const int mid = (lo_e + hi_e + 1) >> 1;
-    if (tstart[mid] <= mg) lo_e = mid; else hi_e = mid - 1;
-  }
-  const int e = lo_e;
-  const int row0 = max(0, p.offsets[e]) + (mg - tstart[e]) * BM;
-  const int nrows = min(BM, min(p.offsets[e + 1], p.R) - row0);
-
-  if (tid < BM) {
-    int ar = -1, fl = -1;
-    if (tid < nrows) {
-      const int i = row0 + tid;
-      fl = p.rows[i];
-      if ((unsigned)fl >= (unsigned)p.R) fl = -1;     // not a valid flat index: padding row
-      else ar = p.a_mode == GG_A_TOKEN ? fl / p.k : (p.a_mode == GG_A_FLAT ? fl : i);
-    }
-    arow[tid] = ar;
-    flat[tid] = fl;
-  }
-
-  // weight rows of this tile
+  const int G = gridDim.x;
+#if defined(GG_ORDER_CONTIG)
+  // workgroup b takes tiles [b*per, (b+1)*per): the N-tiles of an M-tile run back to back
+  // on one CU and share its activation rows through the L2 whatever the dispatch order
+  const int per = (total + G - 1) / G;
+  const int first = blockIdx.x * per, stride = 1, ntiles = min(per, max(total - first, 0));
+#elif defined(GG_ORDER_PLAIN)
+  const int first = blockIdx.x, stride = G, ntiles = (total - first + G - 1) / G;
+#else
+  const int first = xcd_swizzle(blockIdx.x, G), stride = G, ntiles = (total - first + G - 1) / G;
+#endif
   const int64_t RB = (int64_t)(p.K / QK) * FF::BB;  // bytes per stored weight row
-  const uint8_t* wbase0;
-  const uint8_t* wbase1;
-  int n0;
-  if constexpr (STAGE == STAGE_GATEUP) {
-    n0 = nt * (BN / 2);
-    wbase0 = p.w0 + (int64_t)e * p.s0 + (int64_t)n0 * RB;
-    wbase1 = p.w1 + (int64_t)e * p.s1 + (int64_t)n0 * RB;
-  } else {
-    n0 = nt * BN;
-    wbase0 = p.w0 + (int64_t)e * p.s0 + (int64_t)n0 * RB;
-    wbase1 = wbase0;
-  }
-  __syncthreads();
+  const int nchunks = p.K / BK;
 
-  constexpr int AITERS = BM * (BK / 4) / NT;         // float4 per thread per chunk
-  static_assert(AITERS * NT == BM * (BK / 4), "activation chunk split");
-  float4 ar_[AITERS];
-  u32x2 br_[FF::BITERS];
-
-  auto load_chunk = [&](int c) {
-#pragma unroll
-    for (int it = 0; it < AITERS; ++it) {
-      const int idx = it * NT + tid;
-      const int r = idx / (BK / 4), c4 = idx % (BK / 4);
-      const int src = arow[r];
-      ar_[it] = src >= 0 ? *(const float4*)(p.a + (int64_t)src * p.K + c * BK + 4 * c4)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+  // tile L -> expert e (last e with tstart[e] <= M-tile; empty experts share the
+  // next start), first sorted row, rows, N-tile
+  auto decode_tile = [&](int L, int& e, int& row0, int& nrows, int& nt) {
+    const int mg = L / p.n_tiles;
+    nt = L % p.n_tiles;
+    int lo_e = 0, hi_e = E - 1;
+    while (lo_e < hi_e) {
+      const int mid = (lo_e + hi_e + 1) >> 1;
+      if (tstart[mid] <= mg) lo_e = mid; else hi_e = mid - 1;
     }
-#pragma unroll
-    for (int it = 0; it < FF::BITERS; ++it) {
-      const int idx = it * NT + tid;
-      if (idx < FF::BUNITS) {
-        const int r = idx / FF::U8, u = idx % FF::U8;
-        const uint8_t* src;
-        if constexpr (STAGE == STAGE_GATEUP)
-          src = (r < BN / 2 ? wbase0 + (int64_t)r * RB : wbase1 + (int64_t)(r - BN / 2) * RB);
-        else
-          src = wbase0 + (int64_t)r * RB;
-        br_[it] = __builtin_nontemporal_load((const u32x2*)(src + c * FF::CB + 8 * u));
-      }
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int it = 0; it < AITERS; ++it) {
-      const int idx = it * NT + tid;
-      const int r = idx / (BK / 4), c4 = idx % (BK / 4);
-      const float v[4] = {ar_[it].x, ar_[it].y, ar_[it].z, ar_[it].w};
-      _Float16 hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hi[i] = (_Float16)v[i];
-        lo[i] = (_Float16)(v[i] - (float)hi[i]);
-      }
-      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-      *(h4*)(a_hi + r * AS + 4 * c4) = h4{hi[0], hi[1], hi[2], hi[3]};
-      if constexpr (SPLIT) *(h4*)(a_lo + r * AS + 4 * c4) = h4{lo[0], lo[1], lo[2], lo[3]};
-    }
-#pragma unroll
-    for (int it = 0; it < FF::BITERS; ++it) {
-      const int idx = it * NT + tid;
-      if (idx < FF::BUNITS) {
-        const int r = idx / FF::U8, u = idx % FF::U8;
-        *(u32x2*)(bw + r * BS + 8 * u) = br_[it];
-      }
-    }
+    e = lo_e;
+    row0 = offs[e] + (mg - tstart[e]) * BM;
+    nrows = min(BM, offs[e + 1] - row0);
   };
 
-  // wavefront w: n-subtile s uses tile weight rows wrow(s) + lane % 16
+  // wavefront w: n-subtile s uses tile weight rows wrow[s] + lane % 16
   int wrow[2];
   if constexpr (STAGE == STAGE_GATEUP) {
-    wrow[0] = wave * 16;                   // gate columns n0 + 16w ..
+    wrow[0] = wave * 16;                   // gate rows: columns n0 + 16w ..
     wrow[1] = BN / 2 + wave * 16;          // up rows of the same columns
   } else {
     wrow[0] = wave * 32;
@@ -305,73 +250,203 @@ __global__ __launch_bounds__(NT, 2) void grouped_gemm_kernel(Args p) {
   }
   const int ln = lane % 16, lg = lane / 16;
 
-  f32x4 acc[MSUB][2];
+  constexpr int AITERS = BM * (BK / 4) / NT;         // float4 per thread per chunk
+  static_assert(AITERS * NT == BM * (BK / 4), "activation chunk split");
+  // weight units of a half tile (BN/2 rows): unit j is row j / U8, 8-byte unit j % U8, so
+  // consecutive lanes read consecutive bytes; the last partial pass repeats unit HUNITS-1
+  int boff[FF::HITERS], bdst[FF::HITERS];
 #pragma unroll
-  for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nchunks = p.K / BK;
-  load_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
-    store_chunk();
-    __syncthreads();
-    if (c + 1 < nchunks) load_chunk(c + 1);
-#pragma unroll
-    for (int b = 0; b < BKB; ++b) {
-      h8 bf[2];
-      float sc[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint8_t* row = bw + (wrow[s] + ln) * BS;
-        bf[s] = block_frag<FMT>(row, b, lg);
-        sc[s] = block_scale<FMT>(row, b);
-      }
-#pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
-        const int aoff = (m * 16 + ln) * AS + b * QK + 8 * lg;
-        const h8 ahi = *(const h8*)(a_hi + aoff);
-        h8 alo;
-        if constexpr (SPLIT) alo = *(const h8*)(a_lo + aoff);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bf[s], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                              0, 0, 0);
-          if constexpr (SPLIT) part = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bf[s], part, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][s][i] = fmaf(part[i], sc[s], acc[m][s][i]);
-        }
-      }
-    }
-    __syncthreads();
+  for (int it = 0; it < FF::HITERS; ++it) {
+    const int j = min(it * NT + tid, FF::HUNITS - 1);
+    boff[it] = (j / FF::U8) * (int)RB + 8 * (j % FF::U8);
+    bdst[it] = (j / FF::U8) * BS + 8 * (j % FF::U8);
   }
 
-  // ---- epilogue: lane holds rows 16m + 4*lg + i, column ln of each n-subtile ----
-#pragma unroll
-  for (int m = 0; m < MSUB; ++m) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = m * 16 + 4 * lg + i;
-      if (r >= nrows || flat[r] < 0) continue;
-      if constexpr (STAGE == STAGE_GATEUP) {
-        const int f = n0 + wave * 16 + ln;
-        const float g = acc[m][0][i], u = acc[m][1][i];
-        p.h[(int64_t)(row0 + r) * p.N + f] = silu(g) * u;
-      } else {
-        const int fl = flat[r];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int n = n0 + wrow[s] + ln;
-          const float v = acc[m][s][i];
-          if (p.out_mode == GG_OUT_ATOMIC) {
-            const int64_t t = fl / p.k;
-            __hip_atomic_fetch_add(p.out + t * p.N + n, p.topk_w[fl] * v, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-          } else {
-            p.y[(int64_t)fl * p.N + n] = v;
+  for (int k0 = 0; k0 < ntiles; k0 += TW) {
+    // ---- metadata of the window's tiles ----
+    if (tid < TW * BM) {
+      const int w = tid / BM, r = tid % BM;
+      const int L = first + (k0 + w) * stride;
+      int src = 0, fl = -1, tok = 0;
+      float wt = 0.f;
+      if (k0 + w < ntiles) {
+        int e, row0, nrows, nt;
+        decode_tile(L, e, row0, nrows, nt);
+        if (r < nrows) {
+          const int i = row0 + r;
+          const int f = p.rows[i];
+          if ((unsigned)f < (unsigned)p.R) {
+            fl = f;
+            tok = f / p.k;
+            src = p.a_mode == GG_A_TOKEN ? tok : (p.a_mode == GG_A_FLAT ? f : i);
+            if (p.out_mode == GG_OUT_ATOMIC) wt = p.topk_w[f];
           }
         }
       }
+      m_src[w][r] = src;
+      m_flat[w][r] = fl;
+      m_tok[w][r] = tok;
+      m_w[w][r] = wt;
+    }
+    __syncthreads();
+
+    for (int w = 0; w < TW; ++w) {
+      if (k0 + w >= ntiles) break;                    // uniform over the workgroup
+      const int L = first + (k0 + w) * stride;
+      int e, row0, nrows, nt;
+      decode_tile(L, e, row0, nrows, nt);
+      int n0;
+      const uint8_t* hb0;
+      const uint8_t* hb1;
+      if constexpr (STAGE == STAGE_GATEUP) {
+        n0 = nt * (BN / 2);
+        hb0 = p.w0 + (int64_t)e * p.s0 + (int64_t)n0 * RB;          // gate rows
+        hb1 = p.w1 + (int64_t)e * p.s1 + (int64_t)n0 * RB;          // up rows
+      } else {
+        n0 = nt * BN;
+        hb0 = p.w0 + (int64_t)e * p.s0 + (int64_t)n0 * RB;
+        hb1 = hb0 + (int64_t)(BN / 2) * RB;
+      }
+      int aoffs[AITERS];
+#pragma unroll
+      for (int it = 0; it < AITERS; ++it) {
+        const int idx = it * NT + tid;
+        aoffs[it] = m_src[w][idx / (BK / 4)] * p.K + 4 * (idx % (BK / 4));
+      }
+
+      struct Stage {
+        float4 a[AITERS];
+        u32x2 b[2][FF::HITERS];
+      };
+      auto load = [&](int c, Stage& st) {
+#pragma unroll
+        for (int it = 0; it < AITERS; ++it) st.a[it] = *(const float4*)(p.a + aoffs[it] + c * BK);
+        const uint8_t* b0 = hb0 + c * FF::CB;
+        const uint8_t* b1 = hb1 + c * FF::CB;
+#pragma unroll
+        for (int it = 0; it < FF::HITERS; ++it) {
+          st.b[0][it] = *(const u32x2*)(b0 + boff[it]);
+          st.b[1][it] = *(const u32x2*)(b1 + boff[it]);
+        }
+      };
+      auto store = [&](const Stage& st, int buf) {
+#pragma unroll
+        for (int it = 0; it < AITERS; ++it) {
+          const int idx = it * NT + tid;
+          const int r = idx / (BK / 4), c4 = idx % (BK / 4);
+          const float v[4] = {st.a[it].x, st.a[it].y, st.a[it].z, st.a[it].w};
+          _Float16 hi[4], lo[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hi[i] = (_Float16)v[i];
+            lo[i] = (_Float16)(v[i] - (float)hi[i]);
+          }
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+          *(h4*)(a_hi[buf] + r * AS + 4 * c4) = h4{hi[0], hi[1], hi[2], hi[3]};
+          if constexpr (SPLIT) *(h4*)(a_lo[buf] + r * AS + 4 * c4) = h4{lo[0], lo[1], lo[2], lo[3]};
+        }
+#pragma unroll
+        for (int it = 0; it < FF::HITERS; ++it) {
+          *(u32x2*)(bw[buf] + bdst[it]) = st.b[0][it];
+          *(u32x2*)(bw[buf] + (BN / 2) * BS + bdst[it]) = st.b[1][it];
+        }
+      };
+
+      f32x4 acc[MSUB][2];
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      auto compute = [&](int buf) {
+        const _Float16* ah = a_hi[buf];
+        const _Float16* al = a_lo[buf];
+        // blocks in pairs (the parity of a block fixes its byte alignment); one pair's
+        // fragments live at a time
+#pragma unroll 1
+        for (int bp = 0; bp < BKB; bp += 2)
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          const int b = bp + b2;
+          h8 bf[2];
+          float sc[2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const uint8_t* row = bw[buf] + (wrow[s] + ln) * BS;
+            bf[s] = block_frag<FMT>(row, b, lg);
+            sc[s] = block_scale<FMT>(row, b);
+          }
+#pragma unroll
+          for (int m = 0; m < MSUB; ++m) {
+            const int aoff = (m * 16 + ln) * AS + b * QK + 8 * lg;
+            const h8 ahi = *(const h8*)(ah + aoff);
+            h8 alo;
+            if constexpr (SPLIT) alo = *(const h8*)(al + aoff);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  ahi, bf[s], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+              if constexpr (SPLIT)
+                part = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bf[s], part, 0, 0, 0);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[m][s][i] = fmaf(part[i], sc[s], acc[m][s][i]);
+            }
+          }
+        }
+      };
+
+      // Two stages are always in flight at the loop head (chunk indices are clamped
+      // instead of skipping loads), so the compiler's wait counts are exact.
+      Stage s0, s1;
+      load(0, s0);
+      load(min(1, nchunks - 1), s1);
+      int c = 0;
+      for (; c + 2 < nchunks; c += 2) {
+        store(s0, 0);
+        __syncthreads();
+        load(c + 2, s0);
+        compute(0);
+        store(s1, 1);
+        __syncthreads();
+        load(min(c + 3, nchunks - 1), s1);
+        compute(1);
+      }
+      store(s0, 0);                                   // last one or two chunks: no loads
+      __syncthreads();
+      compute(0);
+      if (c + 1 < nchunks) {
+        store(s1, 1);
+        __syncthreads();
+        compute(1);
+      }
+
+      // ---- epilogue: lane holds rows 16m + 4*lg + i, column ln of each n-subtile ----
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m * 16 + 4 * lg + i;
+          const int fl = m_flat[w][r];
+          if (fl < 0) continue;                         // padding row
+          if constexpr (STAGE == STAGE_GATEUP) {
+            const int f = n0 + wave * 16 + ln;
+            const float g = acc[m][0][i], u = acc[m][1][i];
+            p.h[(int64_t)(row0 + r) * p.N + f] = silu(g) * u;
+          } else if (p.out_mode == GG_OUT_ATOMIC) {
+            const float wt = m_w[w][r];
+            float* orow = p.out + (int64_t)m_tok[w][r] * p.N + n0 + ln;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+              __hip_atomic_fetch_add(orow + wrow[s], wt * acc[m][s][i], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            float* yrow = p.y + (int64_t)fl * p.N + n0 + ln;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) yrow[wrow[s]] = acc[m][s][i];
+          }
+        }
+      }
+      __syncthreads();                                  // LDS buffers are reused by the next tile
     }
   }
 }
@@ -385,11 +460,29 @@ __global__ __launch_bounds__(256) void init_out_kernel(float* __restrict__ out,
   ((float4*)out)[i] = residual ? ((const float4*)residual)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return -1;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
 template <int FMT, int STAGE, int MSUB, bool SPLIT>
 static hipError_t launch_t(const Args& a, int64_t R, hipStream_t s) {
   constexpr int BM = 16 * MSUB;
   const int64_t max_m = R / BM + (R < a.E ? R : a.E);
-  const int64_t grid = max_m * a.n_tiles;
+  int64_t grid = max_m * a.n_tiles;                // upper bound of the tile count
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  if (grid > cus) grid = cus;                       // persistent: one workgroup per CU
   hipLaunchKernelGGL((grouped_gemm_kernel<FMT, STAGE, MSUB, SPLIT>), dim3((unsigned)grid), dim3(NT),
                      0, s, a);
   return hipGetLastError();
@@ -405,7 +498,8 @@ static hipError_t launch_f(const Args& a, int64_t R, bool small_m, bool split, h
 }  // namespace gg
 
 bool grouped_supported(const ExpertsDev& W, bool need_gate_up) {
-  if (W.D % 128 || W.F % 128) return false;
+  // down tiles are 256 columns of d_model; K chunks are 128 values
+  if (W.D % 256 || W.F % 128) return false;
   if (W.fmt != MOE_FMT_Q8_0 && W.fmt != MOE_FMT_Q4) return false;
   auto a8 = [](const void* p) { return ((uintptr_t)p & 7) == 0; };
   if (!a8(W.down) || (W.down_stride & 7)) return false;
@@ -434,7 +528,7 @@ hipError_t launch_grouped_gateup(const float* a, int a_mode, const ExpertsDev& W
   p.R = (int)R;
   p.N = W.F;
   p.K = W.D;
-  p.n_tiles = W.F / (gg::BN / 2);
+  p.n_tiles = W.F / (gg::BN / 2);   // 128 columns of h per tile
   p.out_mode = GG_OUT_H;
   p.h = h_sorted;
   const bool sm = grouped_small_m(R);

@@ -10,7 +10,7 @@ namespace moe {
 // Number of D-slices the router GEMV/GEMM is split into, so that small T still
 // spreads the 1 MiB gate over many CUs.  Each slice is a multiple of 32 rows.
 int router_ksplit(int64_t T, int D) {
-  const int64_t tiles = (T + 7) / 8;
+  const int64_t tiles = T >= 32 ? (T + 31) / 32 : (T + 7) / 8;
   int64_t ks = 256 / (tiles > 0 ? tiles : 1);
   if (ks < 1) ks = 1;
   if (ks > D / 32) ks = D / 32;
@@ -68,9 +68,70 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const float* __rest
   }
 }
 
+// Register-tiled fp32 router GEMM for many tokens and E <= 128 experts:
+// part[s][t][e] over the s-th slice of d.  A workgroup owns 32 tokens x 128
+// experts of one slice; each thread accumulates 4 tokens x 4 experts, reading
+// x and G from LDS in 32-row chunks.  G is read from HBM once per token tile
+// (it stays in the L2 across the 32-token tiles of a slice).
+constexpr int RT_T = 32, RT_E = 128, RT_K = 32;
+
+__global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restrict__ x, int64_t T,
+                                                           int D, const float* __restrict__ G,
+                                                           int E, int dchunk,
+                                                           float* __restrict__ part) {
+  __shared__ float xs[RT_K][RT_T + 4];        // [k][token], padded
+  __shared__ __attribute__((aligned(16))) float gs[RT_K][RT_E];
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * RT_T;
+  const int sl = blockIdx.y;
+  const int d0 = sl * dchunk, d1 = min(D, d0 + dchunk);
+  const int tg = tid / 32, eg = tid % 32;     // tokens 4*tg.., experts 4*eg..
+  float acc[4][4] = {};
+  for (int dd = d0; dd < d1; dd += RT_K) {
+    // x chunk: 32 tokens x 32 d (one float per thread-pair step), stored transposed
+    for (int i = tid; i < RT_T * RT_K; i += 256) {
+      const int tt = i / RT_K, c = i % RT_K;
+      const int64_t t = t0 + tt;
+      xs[c][tt] = (t < T && dd + c < d1) ? x[t * D + dd + c] : 0.f;
+    }
+    // G chunk: 32 d x 128 experts
+    for (int i = tid; i < RT_K * RT_E; i += 256) {
+      const int c = i / RT_E, e = i % RT_E;
+      gs[c][e] = (e < E && dd + c < d1) ? G[(int64_t)(dd + c) * E + e] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < RT_K; ++c) {
+      const float4 xv = *(const float4*)&xs[c][4 * tg];
+      const float4 gv = *(const float4*)&gs[c][4 * eg];
+      const float xa[4] = {xv.x, xv.y, xv.z, xv.w}, ga[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], ga[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + 4 * tg + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * eg + j;
+      if (e < E) part[((int64_t)sl * T + t) * E + e] = acc[i][j];
+    }
+  }
+}
+
 hipError_t launch_router_partial(const float* x, int64_t T, int D, const float* G, int E,
                                  float* part, int ksplit, hipStream_t s) {
   const int dchunk = router_dchunk(D, ksplit);
+  if (E <= RT_E && T >= RT_T) {
+    dim3 grid((unsigned)((T + RT_T - 1) / RT_T), (unsigned)ksplit);
+    hipLaunchKernelGGL(router_tiled_kernel, grid, dim3(256), 0, s, x, T, D, G, E, dchunk, part);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((T + 7) / 8), (unsigned)ksplit);
   hipLaunchKernelGGL(router_partial_kernel<8>, grid, dim3(256), 0, s, x, T, D, G, E, dchunk, part);
   return hipGetLastError();
