@@ -139,9 +139,10 @@ moe_status moe_group(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
  * activations enter the matrix cores as two fp16 terms (hi + lo, about fp32
  * accuracy), or as one fp16 rounding with MOE_F_FP16_ACT; |activations| must
  * stay below 65504.  Other shapes take generic fp32 kernels.
- * Combine: without MOE_F_DETERMINISTIC the weighted sum into `out` uses fp32
- * atomics (summation order varies run to run); with it, y is materialised and
- * summed in j order.
+ * Combine: the grouped kernels store y and the weighted sum runs over it in j
+ * order (bit-reproducible); the generic kernels do the same.  The fused
+ * single-token path adds w*y into `out` with fp32 atomics unless
+ * MOE_F_DETERMINISTIC is set.
  *   stage MOE_STAGE_FULL: in = x [T][D]; for row r = t*k + j with e = ids[t][j]:
  *     h = silu(x_t W_gate_e) * (x_t W_up_e), y_r = h W_down_e.
  *   stage MOE_STAGE_DOWN: in = h [T*k][F]; y_r = h_r W_down_e (the routed

@@ -31,6 +31,7 @@ Workspace carve_workspace(void* base, int64_t T, int D, int F, int E, int k, int
   w.h = (float*)take(tk * (size_t)F * sizeof(float));
   w.y = (float*)take(tk * (size_t)D * sizeof(float));
   w.xn = (flags & MOE_F_PRENORM) ? (float*)take((size_t)T * D * sizeof(float)) : nullptr;
+  w.xp = (_Float16*)take((size_t)T * D * 2 * sizeof(_Float16));
   w.bytes = off;
   return w;
 }
@@ -111,22 +112,23 @@ static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const 
                         : "ffn grouped mfma gate/up+down (fp16)")
                : (split ? "ffn grouped mfma down (split fp16)" : "ffn grouped mfma down (fp16)"),
           T, W.D, W.F, W.E, k, W.fmt);
-    const float* h = in;
+    // activations as fp16 planes (hi, lo): x [T][D] in ws.xp, h [R][F] in the h region
+    _Float16* hhi = (_Float16*)ws.h;
+    _Float16* hlo = split ? hhi + (size_t)R * W.F : nullptr;
     int a_mode = GG_A_FLAT;
     if (full) {
-      HIP_TRY(launch_grouped_gateup(in, GG_A_TOKEN, W, offsets, rows, R, k, ws.h, split, s));
-      h = ws.h;
+      _Float16* xhi = ws.xp;
+      _Float16* xlo = split ? xhi + (size_t)T * W.D : nullptr;
+      HIP_TRY(launch_to_planes(in, T * (int64_t)W.D, xhi, xlo, s));
+      HIP_TRY(launch_grouped_gateup(xhi, xlo, GG_A_TOKEN, W, offsets, rows, R, k, hhi, hlo, split,
+                                    s));
       a_mode = GG_A_SORTED;
+    } else {
+      HIP_TRY(launch_to_planes(in, R * (int64_t)W.F, hhi, hlo, s));
     }
     const float* res = (full && (flags & MOE_F_RESIDUAL)) ? in : nullptr;
-    if (out && !y && !(flags & MOE_F_DETERMINISTIC)) {
-      // combine fused into the down epilogue: out starts at the residual (or 0)
-      HIP_TRY(launch_init_out(out, res, T * (int64_t)W.D, s));
-      HIP_TRY(launch_grouped_down(h, a_mode, W, offsets, rows, w, R, k, out, nullptr, split, s));
-      return MOE_OK;
-    }
     float* ybuf = y ? y : ws.y;
-    HIP_TRY(launch_grouped_down(h, a_mode, W, offsets, rows, nullptr, R, k, nullptr, ybuf, split, s));
+    HIP_TRY(launch_grouped_down(hhi, hlo, a_mode, W, offsets, rows, R, k, ybuf, split, s));
     if (out) HIP_TRY(launch_combine(ybuf, w, T, k, W.D, res, out, s));
     return MOE_OK;
   }

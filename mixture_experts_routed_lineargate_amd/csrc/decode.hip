@@ -87,6 +87,7 @@ struct Geo {
   static_assert(PPG * NGRP == FPW && PPG == NWAVE, "one pair per wavefront per group");
   static_assert(GU_ROW % 16 == 0 && DN_ROW % 16 == 0, "16-byte rows");
   static_assert(LDS_BYTES + 16 + 4096 <= 160 * 1024, "LDS budget");
+  static_assert(D * 4 <= 2 * GU_BYTES, "the input row fits in the gate/up region");
   static_assert(F * 4 <= 2 * GU_BYTES, "h staging fits in the gate/up region");
 };
 
@@ -216,15 +217,31 @@ __global__ __launch_bounds__(NT, 1) void decode_layer_kernel(Args p) {
   const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
   const int wg = blockIdx.x;
   const int slot = wg / PARTS, part = wg % PARTS;
+  const bool deterministic = (p.flags & MOE_F_DETERMINISTIC) != 0;
+  const bool router = wg < RW;
+  float* xs = (float*)lds;   // the input row [D]; aliases the gate/up region, free until phase 3
+
+  // ---- issue every load that depends on nothing: x, this workgroup's gate rows, the epoch ----
+  // Router workgroup (eg, ds) multiplies rows 256*ds..+255 of the gate by x for
+  // experts 16*eg..+15; thread (rg, el) takes 8 rows of expert el.
+  // Every workgroup issues the gate loads (the others re-read a router workgroup's rows
+  // from the L2 and drop them): conditional loads would make the wait for x also wait
+  // for them.
+  const float4 xq = ((const float4*)p.x)[tid];
+  const int eg = (wg % RW) % REG, ds = (wg % RW) / REG;
+  const int el = tid % REPG, rg = tid / REPG;
+  const int d0 = ds * (D / RDS) + rg * RROWS;
+  float gq[RROWS];
+#pragma unroll
+  for (int r = 0; r < RROWS; ++r) gq[r] = p.gate[(int64_t)(d0 + r) * E + eg * REPG + el];
   const uint32_t epoch =
       __hip_atomic_load(p.epochs + wg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  const bool deterministic = (p.flags & MOE_F_DETERMINISTIC) != 0;
 
   // ---- input scaling (RMSNorm transition when PRENORM) ----
+  ((float4*)xs)[tid] = xq;
   float inv = 1.f;
   if (p.flags & MOE_F_PRENORM) {
-    const float4 v = ((const float4*)p.x)[tid];
-    float ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    float ss = xq.x * xq.x + xq.y * xq.y + xq.z * xq.z + xq.w * xq.w;
     ss = wave_sum(ss);
     if (lane == 0) red[wave] = ss;
     __syncthreads();
@@ -232,53 +249,44 @@ __global__ __launch_bounds__(NT, 1) void decode_layer_kernel(Args p) {
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) tot += red[w];
     inv = 1.0f / sqrtf(tot / (float)D + PRENORM_EPS);
-    __syncthreads();
+  }
+  __syncthreads();                                  // xs complete; red free again
+
+  // initial value of 8 outputs for the atomic combine, issued as early as possible
+  if (router && !deterministic && tid < D / RW) {
+    const int d = wg * (D / RW) + tid;
+    const float init = (p.flags & MOE_F_RESIDUAL) ? xs[d] * inv : 0.f;
+    __hip_atomic_store(p.out + d, init, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // this lane's 32 activations (block `lane` of the 2048-wide input)
   float xv[QK];
-  {
-    const float4* xp = (const float4*)(p.x + lane * QK);
 #pragma unroll
-    for (int i = 0; i < QK / 4; ++i) {
-      const float4 v = xp[i];
-      xv[4 * i + 0] = v.x * inv;
-      xv[4 * i + 1] = v.y * inv;
-      xv[4 * i + 2] = v.z * inv;
-      xv[4 * i + 3] = v.w * inv;
-    }
+  for (int i = 0; i < QK / 4; ++i) {
+    const float4 v = ((const float4*)xs)[lane * (QK / 4) + i];
+    xv[4 * i + 0] = v.x * inv;
+    xv[4 * i + 1] = v.y * inv;
+    xv[4 * i + 2] = v.z * inv;
+    xv[4 * i + 3] = v.w * inv;
   }
   float xsum = 0.f;
 #pragma unroll
   for (int i = 0; i < QK; ++i) xsum += xv[i];
 
-  // ---- phase 1: partial router logits (+ initial outputs for the atomic combine) ----
-  // Router workgroup (eg, ds) multiplies rows 256*ds..+255 of the gate by x for
-  // experts 16*eg..+15; x is scaled by the RMSNorm factor afterwards (linear).
-  if (wg < RW) {
-    const int eg = wg % REG, ds = wg / REG;
-    const int el = tid % REPG, rg = tid / REPG;
-    const int e = eg * REPG + el;
-    const int d0 = ds * (D / RDS) + rg * RROWS;
+  // ---- phase 1: partial router logits (x is scaled by the RMSNorm factor afterwards) ----
+  if (router) {
     float acc = 0.f;
 #pragma unroll
-    for (int r = 0; r < RROWS; ++r) {
-      const int d = d0 + r;
-      acc = fmaf(p.x[d], p.gate[(int64_t)d * E + e], acc);
-    }
+    for (int r = 0; r < RROWS; ++r) acc = fmaf(xs[d0 + r], gq[r], acc);
     red[tid] = acc;
-    if (!deterministic && tid < D / RW) {
-      const int d = wg * (D / RW) + tid;
-      const float init = (p.flags & MOE_F_RESIDUAL) ? p.x[d] * inv : 0.f;
-      __hip_atomic_store(p.out + d, init, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
     __syncthreads();
     if (tid < REPG) {
-      float s = 0.f;
-      for (int g = 0; g < RGRP; ++g) s += red[g * REPG + tid];
-      rsum[tid] = s * inv;
+      float sum = 0.f;
+      for (int g = 0; g < RGRP; ++g) sum += red[g * REPG + tid];
+      rsum[tid] = sum * inv;
     }
-    // the output initialisation must land before any partial of this workgroup is visible
+    // the output initialisation must land before any partial of this workgroup is
+    // visible (it was issued long before, so this wait is short)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     {
@@ -369,19 +377,18 @@ __global__ __launch_bounds__(NT, 1) void decode_layer_kernel(Args p) {
   for (int g = 0; g < G::NGRP; ++g) {
 #pragma unroll
     for (int it = 0; it < G::GRP_ITERS; ++it) {
-      const int c = it * NT + tid;
-      if (c < G::GRP_CHUNKS) {
-        constexpr int half = G::GRP_CHUNKS / 2;       // gate rows first, then up rows
-        const int64_t row_off = (int64_t)(g * G::PPG) * G::GU_ROW;
-        const uint8_t* src = c < half ? gsrc + row_off + 16 * c : usrc + row_off + 16 * (c - half);
-        gu[g][it] = __builtin_nontemporal_load((const u32x4*)src);
-      }
+      // unconditional (clamped) loads keep the compiler's wait counts exact
+      const int c = min(it * NT + tid, G::GRP_CHUNKS - 1);
+      constexpr int half = G::GRP_CHUNKS / 2;         // gate rows first, then up rows
+      const int64_t row_off = (int64_t)(g * G::PPG) * G::GU_ROW;
+      const uint8_t* src = c < half ? gsrc + row_off + 16 * c : usrc + row_off + 16 * (c - half);
+      gu[g][it] = __builtin_nontemporal_load((const u32x4*)src);
     }
   }
 #pragma unroll
   for (int it = 0; it < G::DN_ITERS; ++it) {
-    const int c = it * NT + tid;
-    if (c < G::DN_CHUNKS) dn[it] = __builtin_nontemporal_load((const u32x4*)(dsrc + 16 * c));
+    const int c = min(it * NT + tid, G::DN_CHUNKS - 1);
+    dn[it] = __builtin_nontemporal_load((const u32x4*)(dsrc + 16 * c));
   }
 #pragma unroll
   for (int g = 0; g < G::NGRP; ++g) {

@@ -110,24 +110,51 @@ hipError_t launch_down_generic(const float* h, const ExpertsDev& W, const int32_
 }
 
 // out[t][d] = sum_j w[t][j] * y[t*k+j][d] (j ascending) (+ residual[t][d]).
+// Four outputs per thread when every row is 16-byte aligned (D % 4 == 0 and
+// aligned bases), one otherwise; the summation order is the same either way.
+template <int V>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const float* __restrict__ w, int64_t T,
                                                       int k, int D,
                                                       const float* __restrict__ residual,
                                                       float* __restrict__ out) {
   const int64_t t = blockIdx.x;
-  const int d = blockIdx.y * 256 + threadIdx.x;
+  const int d = (blockIdx.y * 256 + threadIdx.x) * V;
   if (d >= D) return;
-  float s = 0.f;
-  for (int j = 0; j < k; ++j) s = fmaf(w[t * k + j], y[(t * k + j) * D + d], s);
-  if (residual) s += residual[t * D + d];
-  out[t * D + d] = s;
+  float s[V] = {};
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[t * k + j];
+    const float* yr = y + (t * k + j) * D + d;
+    if constexpr (V == 4) {
+      const float4 v = *(const float4*)yr;
+      s[0] = fmaf(wj, v.x, s[0]);
+      s[1] = fmaf(wj, v.y, s[1]);
+      s[2] = fmaf(wj, v.z, s[2]);
+      s[3] = fmaf(wj, v.w, s[3]);
+    } else {
+      s[0] = fmaf(wj, yr[0], s[0]);
+    }
+  }
+  if (residual) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) s[i] += residual[t * D + d + i];
+  }
+  if constexpr (V == 4)
+    *(float4*)(out + t * D + d) = make_float4(s[0], s[1], s[2], s[3]);
+  else
+    out[t * D + d] = s[0];
 }
 
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int D,
                           const float* residual, float* out, hipStream_t s) {
-  dim3 grid((unsigned)T, (unsigned)((D + 255) / 256));
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, y, w, T, k, D, residual, out);
+  auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
+  if (D % 4 == 0 && a16(y) && a16(out) && a16(residual)) {
+    dim3 grid((unsigned)T, (unsigned)((D / 4 + 255) / 256));
+    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, s, y, w, T, k, D, residual, out);
+  } else {
+    dim3 grid((unsigned)T, (unsigned)((D + 255) / 256));
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, s, y, w, T, k, D, residual, out);
+  }
   return hipGetLastError();
 }
 

@@ -6,31 +6,36 @@
 // new routing sort).  Two stages:
 //
 //   gate/up  h[i][f] = silu(a_i . Wg_e[:, f]) * (a_i . Wu_e[:, f])   (K = d_model)
-//   down     y[i][n] = a_i . Wd_e[:, n]                              (K = d_ff)
-//            combined as out[t][n] += w_{t,j} y[i][n] (fp32 atomics), or
-//            stored as y[flat][n] for an ordered combine.
+//   down     y[flat][n] = a_i . Wd_e[:, n]                           (K = d_ff)
+//
+// The weighted combine reads y afterwards in slot order (a plain store of y
+// and one pass over it moves fewer bytes per second of GPU time than fp32
+// atomic adds into the output: ~13 us of stores plus a read pass, against
+// ~50 us for the 16.8M atomics of a 1024-token microbatch), so the result is
+// bit-reproducible.
 //
 // Tiles.  A workgroup (4 wavefronts) owns BM = 16*MSUB rows of one expert and
-// 128 weight rows (down: 128 output columns; gate/up: 64 gate + 64 up rows of
-// the same 64 columns of h, so the SwiGLU epilogue is lane-local).  The tile
-// list is not materialised: each workgroup reads expert_offsets, scans the
-// per-expert tile counts in one wavefront and finds its own (expert, M-tile,
-// N-tile), so the grid is sized for the worst case and surplus workgroups exit
-// at once.  Workgroups are numbered so that consecutive tiles (the N-tiles of
-// one M-tile, then the next M-tile of the same expert) land on the same XCD
-// (dispatch is round-robin over the 8 XCDs), where they share activation rows
-// and weight tiles through that XCD's L2.
+// 256 weight rows (down: 256 output columns; gate/up: 128 gate + 128 up rows of
+// the same 128 columns of h, so the SwiGLU epilogue is lane-local); each
+// wavefront computes 64 rows x 64 weight rows.  The tile list is not
+// materialised: each workgroup reads expert_offsets, scans the per-expert tile
+// counts in one wavefront and walks its own tiles.  Two workgroups share a CU.
 //
-// K loop: chunks of 4 blocks (128 values).  Each chunk of activations (fp32)
-// and raw weight blocks is prefetched into registers while the previous chunk
-// is multiplied, then written to LDS: activations as fp16 (x = hi + lo with two
-// fp16 terms unless the single-rounding variant is asked for), weight blocks
-// byte-for-byte.  Weights enter the MFMA as exact small integers (q for Q8_0,
-// q - 8 for 4-bit, both exact in fp16) built with the 0x6400 exponent trick;
-// one v_mfma_f32_16x16x32_f16 covers exactly one 32-value block, and its fp32
-// result is scaled by that block's fp16 scale into the fp32 accumulator.  So
-// the only roundings are those of the activations (none beyond fp32 with the
-// split) and fp32 accumulation.
+// Operands.  Activations arrive as fp16 planes (a = hi + lo, or hi alone when
+// single rounding is asked for), converted once per call rather than per tile.
+// Weights enter the MFMA as an exact pair of fp16 values per weight: the block
+// code q (or q - 8) is rebuilt as fp16 with the 0x6400 exponent trick, then
+// hi = fp16(d*q) and lo = fma(q, d, -hi), which is exact because d*q has at most
+// 19 significant bits.  So every MFMA accumulates straight into the fp32
+// accumulator (no per-block scaling pass): per 32-value block
+// acc += a_hi*(w_hi + w_lo) (+ a_lo*w_hi), and the only roundings are those of
+// the activations and fp32 accumulation.
+//
+// K loop: chunks of 2 blocks (64 values), prefetched into registers two chunks
+// ahead with unconditional loads, then written to one LDS buffer: activation
+// 16-byte pieces XOR-swizzled by row (conflict-free fragment reads), weight rows
+// transposed into dword slabs (thread t loads row t; padded slab stride keeps the
+// four lane groups of a fragment in distinct banks).
 #include "internal.hpp"
 
 namespace moe {
@@ -39,21 +44,22 @@ namespace gg {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 512;               // threads per workgroup (8 wavefronts, one workgroup per CU)
+constexpr int NT = 256;               // threads per workgroup (4 wavefronts, two workgroups per CU)
 constexpr int NW = NT / WAVE;
-constexpr int BN = 256;               // weight rows per tile (32 per wavefront)
-constexpr int BKB = 4;                // blocks per K chunk
-constexpr int BK = BKB * QK;          // 128 values per K chunk
-constexpr int AS = BK + 8;            // fp16 per LDS activation row (272 B: conflict-free b128 reads)
+constexpr int BN = 256;               // weight rows per tile (64 per wavefront)
+constexpr int BKB = 2;                // blocks per K chunk
+constexpr int BK = BKB * QK;          // 64 values per K chunk
+constexpr int WG_PER_CU = 2;
 
 enum { STAGE_GATEUP = 0, STAGE_DOWN = 1 };
 
 struct Args {
-  const float* a;            // activations fp32, row length K
+  const _Float16* ahi;       // activations as fp16 planes: a = ahi + alo (alo unused when
+  const _Float16* alo;       //   activations are single-rounded), rows of length K
   const int32_t* rows;       // sorted_rows [R]
   const int32_t* offsets;    // expert_offsets [E+1]
-  const float* topk_w;       // [R] flat (t*k + j), OUT_ATOMIC only
   int k;                     // top-k (token = flat / k)
   int a_mode;                // GG_A_*
   const uint8_t* w0;         // gate (gate/up stage) or down
@@ -63,20 +69,22 @@ struct Args {
   int E, N, K;               // N = output columns (d_ff for gate/up, d_model for down)
   int R;                     // rows (T * k); offsets and rows are clamped to it
   int n_tiles;
-  int out_mode;              // GG_OUT_*
-  float* h;                  // GG_OUT_H: [R][N] in sorted order
-  float* out;                // GG_OUT_ATOMIC: [T][N]
-  float* y;                  // GG_OUT_Y: [R][N] in flat order
+  _Float16* ohi;             // gate/up: h planes [R][N] in sorted order
+  _Float16* olo;
+  float* y;                  // down: y [R][N] in flat order
 };
 
+// A chunk of weight rows sits in LDS transposed: slab u holds dword u of all
+// BN rows (thread t loads row t, one dword per slab), slabs SLAB dwords apart.
+// SLAB = 256 + 8 (Q8_0) / 256 + 16 (4-bit) puts the dwords that the four lane
+// groups of a fragment read (2 / 1 dwords apart) in distinct banks.
 template <int FMT>
 struct Fmt {
   static constexpr int BB = FMT == MOE_FMT_Q8_0 ? 34 : 18;
-  static constexpr int CB = BKB * BB;          // bytes of one row in one K chunk (136 / 72)
-  static constexpr int U8 = CB / 8;            // 8-byte units per row chunk (17 / 9)
-  static constexpr int HUNITS = BN / 2 * U8;   // 8-byte units of half a tile's rows
-  static constexpr int HITERS = (HUNITS + NT - 1) / NT;
-  static_assert(CB % 8 == 0, "row chunks are 8-byte multiples");
+  static constexpr int CB = BKB * BB;          // bytes of one row in one K chunk (68 / 36)
+  static constexpr int U4 = CB / 4;            // dwords per row chunk = dword loads per thread
+  static constexpr int SLAB = BN + (FMT == MOE_FMT_Q8_0 ? 8 : 16);
+  static_assert(CB % 4 == 0 && BN == NT, "one weight row per thread, whole dwords");
 };
 
 __device__ inline int xcd_swizzle(int bid, int total) {
@@ -86,21 +94,14 @@ __device__ inline int xcd_swizzle(int bid, int total) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + s;
 }
 
-__device__ inline uint32_t lds32(const uint8_t* p, int off) { return *(const uint32_t*)(p + off); }
-
-// Scale of block b of an LDS weight row (fp16 at byte 0 of the block).
+// Dword at byte offset off (a multiple of 4) of a weight row stored as a column
+// of the slab layout.
 template <int FMT>
-__device__ inline float block_scale(const uint8_t* row, int b) {
-  constexpr int BB = Fmt<FMT>::BB;
-  const int ob = b * BB;                               // b*BB = 2b mod 4
-  const uint32_t w = lds32(row, ob & ~3);
-  const uint16_t bits = (ob & 2) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
-  return half_bits_to_float(bits);
-}
+__device__ inline uint32_t wdw(const uint32_t* col, int off) { return col[(off >> 2) * Fmt<FMT>::SLAB]; }
 
 // The 8 weights k = 8g .. 8g+7 of block b as exact fp16 (q, or q - 8).
 template <int FMT>
-__device__ inline h8 block_frag(const uint8_t* row, int b, int g) {
+__device__ inline h8 block_frag(const uint32_t* col, int b, int g) {
   constexpr int BB = Fmt<FMT>::BB;
   union {
     uint32_t u[4];
@@ -111,12 +112,12 @@ __device__ inline h8 block_frag(const uint8_t* row, int b, int g) {
     const int s = b * BB + 2 + 8 * g;                  // 2 mod 4 when b is even
     uint32_t q0, q1;
     if (s & 2) {
-      const uint32_t d0 = lds32(row, s - 2), d1 = lds32(row, s + 2), d2 = lds32(row, s + 6);
+      const uint32_t d0 = wdw<FMT>(col, s - 2), d1 = wdw<FMT>(col, s + 2), d2 = wdw<FMT>(col, s + 6);
       q0 = __builtin_amdgcn_alignbyte(d1, d0, 2);
       q1 = __builtin_amdgcn_alignbyte(d2, d1, 2);
     } else {
-      q0 = lds32(row, s);
-      q1 = lds32(row, s + 4);
+      q0 = wdw<FMT>(col, s);
+      q1 = wdw<FMT>(col, s + 4);
     }
     // two's complement -> biased unsigned, then 0x64uu = 1024 + u as fp16
     q0 ^= 0x80808080u;
@@ -132,9 +133,9 @@ __device__ inline h8 block_frag(const uint8_t* row, int b, int g) {
     const int s = b * BB + 2 + 4 * g;                  // 2 mod 4 when b is even
     uint32_t n;
     if (s & 2) {
-      n = __builtin_amdgcn_alignbyte(lds32(row, s + 2), lds32(row, s - 2), 2);
+      n = __builtin_amdgcn_alignbyte(wdw<FMT>(col, s + 2), wdw<FMT>(col, s - 2), 2);
     } else {
-      n = lds32(row, s);
+      n = wdw<FMT>(col, s);
     }
     // byte j holds element 2j (low nibble) and 2j+1 (high nibble)
     const uint32_t lo = n & 0x0f0f0f0fu, hi = (n >> 4) & 0x0f0f0f0fu;
@@ -149,39 +150,74 @@ __device__ inline h8 block_frag(const uint8_t* row, int b, int g) {
   return r.v;
 }
 
-constexpr int TW = 8;                  // tiles per metadata window
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return -1;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+// Block b's 8 weights k = 8g .. 8g+7 as an exact pair of fp16 vectors: d*q = hi + lo
+// with hi = fp16(d*q) and lo = d*q - hi (d*q has at most 19 significant bits, so lo
+// is exact; needs |d*q| < 65504, i.e. |d| < 511 for Q8_0 and |d| < 8187 for 4-bit).
+template <int FMT>
+__device__ inline void block_frag_hl(const uint32_t* col, int b, int g, h8& hi, h8& lo) {
+  const h8 q = block_frag<FMT>(col, b, g);
+  constexpr int BB = Fmt<FMT>::BB;
+  const int ob = b * BB;
+  const uint32_t w = wdw<FMT>(col, ob & ~3);
+  const uint16_t bits = (ob & 2) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+  const _Float16 d = __builtin_bit_cast(_Float16, bits);
+  const h8 dd = {d, d, d, d, d, d, d, d};
+  hi = q * dd;
+  lo = __builtin_elementwise_fma(q, dd, -hi);
+}
 
 // Persistent: each workgroup walks tiles L = slot, slot + G, ... where slot()
 // gives the workgroups of one XCD consecutive tiles (tiles are numbered M-tile
-// major, so an XCD works on a few M-tiles x all their N-tiles at a time and
-// shares activation rows and weight tiles in its L2).
+// major, so an XCD works on a few M-tiles x their N-tiles at a time and can
+// share activation rows and weight tiles in its L2).
 //
-// Row metadata (activation row, token, combine weight) of a window of TW tiles
-// is fetched into LDS in one batch, so the dependent index loads cost one round
-// trip per window rather than per tile.  Every load of the K loop is
-// unconditional (padding rows read a valid row and are never stored), so the
-// compiler's wait counts stay exact and the two-chunk prefetch is not drained.
+// Row metadata (activation row, flat row) of a window of TW tiles is fetched
+// into LDS in one batch, so the dependent index loads cost one round trip per
+// window rather than per tile.
 //
-// K pipeline: two register stages and two LDS buffers.  Chunk c+2 is fetched
-// while chunk c is multiplied; one barrier per chunk.
+// K pipeline: activations (fp16 planes) and raw weight blocks go from global
+// memory straight into one of two LDS buffers (global_load_lds), two chunks in
+// flight.  Every wavefront issues exactly the same number of loads per chunk,
+// so an explicit vmcnt wait names the chunk that must have landed; plain
+// s_barrier is used in the loop because __syncthreads would also wait for the
+// chunk still in flight.
+//
+// Wavefront w computes 64 rows x 64 weight rows (4 x 4 MFMA tiles): down rows
+// 64w .. 64w+63, or gate rows 32w .. 32w+31 (subtiles 0, 1) and the up rows
+// of the same columns (subtiles 2, 3).  Activation chunks are stored in LDS
+// with their 16-byte pieces XOR-swizzled by row, so the 16 rows a fragment
+// read touches fall in distinct banks.
 template <int FMT, int STAGE, int MSUB, bool SPLIT>
-__global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Args p) {
+__global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
   using FF = Fmt<FMT>;
   constexpr int BM = 16 * MSUB;
-  constexpr int BS = FF::CB;                        // LDS bytes per weight row
-  constexpr int A_ELEMS = BM * AS;
-  constexpr int B_BYTES = BN * BS + 16;             // +16: aligned reads may pass the end
-  static_assert(TW * BM <= NT, "one metadata entry per thread");
-  __shared__ __attribute__((aligned(16))) _Float16 a_hi[2][A_ELEMS];
-  __shared__ __attribute__((aligned(16))) _Float16 a_lo[2][SPLIT ? A_ELEMS : 8];
-  __shared__ __attribute__((aligned(16))) uint8_t bw[2][B_BYTES];
+  constexpr int TW = NT / BM;                       // tiles per metadata window
+  constexpr int PL = SPLIT ? 2 : 1;                 // activation planes
+  constexpr int A_BYTES = BM * BK * 2;              // one plane of one chunk
+  constexpr int A_DMA = BM * (BK / 8) >= NT ? BM * (BK / 8) / NT : 1;   // 16-byte loads / plane
+  constexpr int B_BYTES = FF::U4 * FF::SLAB * 4;
+  constexpr int BUF = PL * A_BYTES + B_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[BUF];
   __shared__ int offs[MAX_E + 1];                   // expert_offsets clamped to [0, R]
   __shared__ int tstart[MAX_E + 1];                 // M-tiles of experts < e
   __shared__ int total_m;
   __shared__ int m_src[TW][BM];                     // activation row (always a valid row)
   __shared__ int m_flat[TW][BM];                    // flat row t*k+j, -1 = padding
-  __shared__ int m_tok[TW][BM];                     // token of the row
-  __shared__ float m_w[TW][BM];                     // combine weight of the row
 
   const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
   const int E = p.E;
@@ -211,25 +247,15 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Args p) {
   __syncthreads();
   const int total = total_m * p.n_tiles;
   const int G = gridDim.x;
-#if defined(GG_ORDER_CONTIG)
-  // workgroup b takes tiles [b*per, (b+1)*per): the N-tiles of an M-tile run back to back
-  // on one CU and share its activation rows through the L2 whatever the dispatch order
-  const int per = (total + G - 1) / G;
-  const int first = blockIdx.x * per, stride = 1, ntiles = min(per, max(total - first, 0));
-#elif defined(GG_ORDER_PLAIN)
-  const int first = blockIdx.x, stride = G, ntiles = (total - first + G - 1) / G;
-#else
-  const int first = xcd_swizzle(blockIdx.x, G), stride = G, ntiles = (total - first + G - 1) / G;
-#endif
+  const int first = xcd_swizzle(blockIdx.x, G);
+  const int ntiles = (total - first + G - 1) / G;
   const int64_t RB = (int64_t)(p.K / QK) * FF::BB;  // bytes per stored weight row
-  const int nchunks = p.K / BK;
+  const int nchunks = p.K / BK;                     // even (K is a multiple of 128)
 
-  // tile L -> expert e (last e with tstart[e] <= M-tile; empty experts share the
-  // next start), first sorted row, rows, N-tile
   auto decode_tile = [&](int L, int& e, int& row0, int& nrows, int& nt) {
     const int mg = L / p.n_tiles;
     nt = L % p.n_tiles;
-    int lo_e = 0, hi_e = E - 1;
+    int lo_e = 0, hi_e = E - 1;                     // last e with tstart[e] <= mg
     while (lo_e < hi_e) {
       const int mid = (lo_e + hi_e + 1) >> 1;
       if (tstart[mid] <= mg) lo_e = mid; else hi_e = mid - 1;
@@ -239,62 +265,45 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Args p) {
     nrows = min(BM, offs[e + 1] - row0);
   };
 
-  // wavefront w: n-subtile s uses tile weight rows wrow[s] + lane % 16
-  int wrow[2];
-  if constexpr (STAGE == STAGE_GATEUP) {
-    wrow[0] = wave * 16;                   // gate rows: columns n0 + 16w ..
-    wrow[1] = BN / 2 + wave * 16;          // up rows of the same columns
-  } else {
-    wrow[0] = wave * 32;
-    wrow[1] = wave * 32 + 16;
+  // tile weight row of n-subtile s of this wavefront
+  int wrow[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if constexpr (STAGE == STAGE_GATEUP)
+      wrow[s] = (s < 2 ? 0 : BN / 2) + wave * 32 + (s & 1) * 16;
+    else
+      wrow[s] = wave * 64 + s * 16;
   }
   const int ln = lane % 16, lg = lane / 16;
 
-  constexpr int AITERS = BM * (BK / 4) / NT;         // float4 per thread per chunk
-  static_assert(AITERS * NT == BM * (BK / 4), "activation chunk split");
-  // weight units of a half tile (BN/2 rows): unit j is row j / U8, 8-byte unit j % U8, so
-  // consecutive lanes read consecutive bytes; the last partial pass repeats unit HUNITS-1
-  int boff[FF::HITERS], bdst[FF::HITERS];
-#pragma unroll
-  for (int it = 0; it < FF::HITERS; ++it) {
-    const int j = min(it * NT + tid, FF::HUNITS - 1);
-    boff[it] = (j / FF::U8) * (int)RB + 8 * (j % FF::U8);
-    bdst[it] = (j / FF::U8) * BS + 8 * (j % FF::U8);
-  }
-
   for (int k0 = 0; k0 < ntiles; k0 += TW) {
     // ---- metadata of the window's tiles ----
-    if (tid < TW * BM) {
+    {
       const int w = tid / BM, r = tid % BM;
-      const int L = first + (k0 + w) * stride;
-      int src = 0, fl = -1, tok = 0;
-      float wt = 0.f;
-      if (k0 + w < ntiles) {
+      int src = 0, fl = -1;
+      if (w < TW && k0 + w < ntiles) {
         int e, row0, nrows, nt;
-        decode_tile(L, e, row0, nrows, nt);
+        decode_tile(first + (k0 + w) * G, e, row0, nrows, nt);
         if (r < nrows) {
           const int i = row0 + r;
           const int f = p.rows[i];
           if ((unsigned)f < (unsigned)p.R) {
             fl = f;
-            tok = f / p.k;
-            src = p.a_mode == GG_A_TOKEN ? tok : (p.a_mode == GG_A_FLAT ? f : i);
-            if (p.out_mode == GG_OUT_ATOMIC) wt = p.topk_w[f];
+            src = p.a_mode == GG_A_TOKEN ? f / p.k : (p.a_mode == GG_A_FLAT ? f : i);
           }
         }
       }
-      m_src[w][r] = src;
-      m_flat[w][r] = fl;
-      m_tok[w][r] = tok;
-      m_w[w][r] = wt;
+      if (w < TW) {
+        m_src[w][r] = src;
+        m_flat[w][r] = fl;
+      }
     }
     __syncthreads();
 
     for (int w = 0; w < TW; ++w) {
       if (k0 + w >= ntiles) break;                    // uniform over the workgroup
-      const int L = first + (k0 + w) * stride;
       int e, row0, nrows, nt;
-      decode_tile(L, e, row0, nrows, nt);
+      decode_tile(first + (k0 + w) * G, e, row0, nrows, nt);
       int n0;
       const uint8_t* hb0;
       const uint8_t* hb1;
@@ -307,117 +316,109 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Args p) {
         hb0 = p.w0 + (int64_t)e * p.s0 + (int64_t)n0 * RB;
         hb1 = hb0 + (int64_t)(BN / 2) * RB;
       }
-      int aoffs[AITERS];
+      // activation 16-byte pieces of this thread: slot q = i*NT + tid (mod the slots of a
+      // plane) is row q / 8, stored piece q % 8, holding logical piece (q % 8) ^ swz(row)
+      int64_t aoff[A_DMA];
 #pragma unroll
-      for (int it = 0; it < AITERS; ++it) {
-        const int idx = it * NT + tid;
-        aoffs[it] = m_src[w][idx / (BK / 4)] * p.K + 4 * (idx % (BK / 4));
+      for (int i = 0; i < A_DMA; ++i) {
+        const int q = (i * NT + tid) % (BM * (BK / 8));
+        const int r = q / 8, c = (q % 8) ^ ((r >> 1) & 7);
+        aoff[i] = (int64_t)m_src[w][r] * p.K + 8 * c;
       }
 
+      const uint8_t* brow = tid < BN / 2 ? hb0 + (int64_t)tid * RB : hb1 + (int64_t)(tid - BN / 2) * RB;
       struct Stage {
-        float4 a[AITERS];
-        u32x2 b[2][FF::HITERS];
+        u32x4 a[PL][A_DMA];
+        uint32_t b[FF::U4];
       };
       auto load = [&](int c, Stage& st) {
 #pragma unroll
-        for (int it = 0; it < AITERS; ++it) st.a[it] = *(const float4*)(p.a + aoffs[it] + c * BK);
-        const uint8_t* b0 = hb0 + c * FF::CB;
-        const uint8_t* b1 = hb1 + c * FF::CB;
+        for (int pl = 0; pl < PL; ++pl) {
+          const _Float16* src = (pl ? p.alo : p.ahi) + c * BK;
 #pragma unroll
-        for (int it = 0; it < FF::HITERS; ++it) {
-          st.b[0][it] = *(const u32x2*)(b0 + boff[it]);
-          st.b[1][it] = *(const u32x2*)(b1 + boff[it]);
+          for (int i = 0; i < A_DMA; ++i) st.a[pl][i] = *(const u32x4*)(src + aoff[i]);
         }
+        const uint32_t* bsrc = (const uint32_t*)(brow + c * FF::CB);
+#pragma unroll
+        for (int u = 0; u < FF::U4; ++u) st.b[u] = bsrc[u];
       };
-      auto store = [&](const Stage& st, int buf) {
+      auto store = [&](const Stage& st) {
 #pragma unroll
-        for (int it = 0; it < AITERS; ++it) {
-          const int idx = it * NT + tid;
-          const int r = idx / (BK / 4), c4 = idx % (BK / 4);
-          const float v[4] = {st.a[it].x, st.a[it].y, st.a[it].z, st.a[it].w};
-          _Float16 hi[4], lo[4];
+        for (int pl = 0; pl < PL; ++pl)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hi[i] = (_Float16)v[i];
-            lo[i] = (_Float16)(v[i] - (float)hi[i]);
-          }
-          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-          *(h4*)(a_hi[buf] + r * AS + 4 * c4) = h4{hi[0], hi[1], hi[2], hi[3]};
-          if constexpr (SPLIT) *(h4*)(a_lo[buf] + r * AS + 4 * c4) = h4{lo[0], lo[1], lo[2], lo[3]};
-        }
+          for (int i = 0; i < A_DMA; ++i)
+            *(u32x4*)(lds + pl * A_BYTES + ((i * NT + tid) % (BM * (BK / 8))) * 16) = st.a[pl][i];
+        uint32_t* bw = (uint32_t*)(lds + PL * A_BYTES) + tid;     // weight row tid
 #pragma unroll
-        for (int it = 0; it < FF::HITERS; ++it) {
-          *(u32x2*)(bw[buf] + bdst[it]) = st.b[0][it];
-          *(u32x2*)(bw[buf] + (BN / 2) * BS + bdst[it]) = st.b[1][it];
-        }
+        for (int u = 0; u < FF::U4; ++u) bw[u * FF::SLAB] = st.b[u];
       };
 
-      f32x4 acc[MSUB][2];
+      f32x4 acc[MSUB][4];
 #pragma unroll
       for (int m = 0; m < MSUB; ++m)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      auto compute = [&](int buf) {
-        const _Float16* ah = a_hi[buf];
-        const _Float16* al = a_lo[buf];
-        // blocks in pairs (the parity of a block fixes its byte alignment); one pair's
-        // fragments live at a time
-#pragma unroll 1
-        for (int bp = 0; bp < BKB; bp += 2)
+      // Per block: acc += a_hi (w_hi + w_lo) [+ a_lo w_hi].  The dropped a_lo * w_lo
+      // term is below 2^-22 of the product.
+      auto compute = [&](const uint8_t* buf) {
+        const uint32_t* bw = (const uint32_t*)(buf + PL * A_BYTES);
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-          const int b = bp + b2;
-          h8 bf[2];
-          float sc[2];
+        for (int b = 0; b < BKB; ++b) {
+          h8 bh[4], bl[4];
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const uint8_t* row = bw[buf] + (wrow[s] + ln) * BS;
-            bf[s] = block_frag<FMT>(row, b, lg);
-            sc[s] = block_scale<FMT>(row, b);
-          }
+          for (int s = 0; s < 4; ++s) block_frag_hl<FMT>(bw + wrow[s] + ln, b, lg, bh[s], bl[s]);
+          h8 ah[MSUB], al[MSUB];
 #pragma unroll
           for (int m = 0; m < MSUB; ++m) {
-            const int aoff = (m * 16 + ln) * AS + b * QK + 8 * lg;
-            const h8 ahi = *(const h8*)(ah + aoff);
-            h8 alo;
-            if constexpr (SPLIT) alo = *(const h8*)(al + aoff);
+            const int r = m * 16 + ln;
+            const int o = r * (BK * 2) + ((((QK / 8) * b + lg) ^ ((r >> 1) & 7)) * 16);
+            ah[m] = *(const h8*)(buf + o);
+            if constexpr (SPLIT) al[m] = *(const h8*)(buf + A_BYTES + o);
+          }
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  ahi, bf[s], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-              if constexpr (SPLIT)
-                part = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bf[s], part, 0, 0, 0);
+          for (int m = 0; m < MSUB; ++m)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[m][s][i] = fmaf(part[i], sc[s], acc[m][s][i]);
-            }
+            for (int s = 0; s < 4; ++s)
+              acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bh[s], acc[m][s], 0, 0, 0);
+#pragma unroll
+          for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bl[s], acc[m][s], 0, 0, 0);
+          if constexpr (SPLIT) {
+#pragma unroll
+            for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+              for (int s = 0; s < 4; ++s)
+                acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[m], bh[s], acc[m][s], 0, 0, 0);
           }
         }
       };
 
-      // Two stages are always in flight at the loop head (chunk indices are clamped
-      // instead of skipping loads), so the compiler's wait counts are exact.
+      // Two register stages are in flight at the loop head (chunk indices are clamped
+      // instead of skipping loads, so the compiler's wait counts stay exact); the LDS
+      // buffer is written, multiplied, and released once per chunk.
+      // (sched_barrier keeps each stage's loads together, so waiting for one stage
+      // never waits for the other)
       Stage s0, s1;
       load(0, s0);
-      load(min(1, nchunks - 1), s1);
-      int c = 0;
-      for (; c + 2 < nchunks; c += 2) {
-        store(s0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(1, s1);                                    // nchunks is even
+      __builtin_amdgcn_sched_barrier(0);
+      for (int c = 0; c < nchunks; c += 2) {
+        store(s0);
         __syncthreads();
-        load(c + 2, s0);
-        compute(0);
-        store(s1, 1);
+        load(min(c + 2, nchunks - 1), s0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(lds);
+        __syncthreads();
+        store(s1);
         __syncthreads();
         load(min(c + 3, nchunks - 1), s1);
-        compute(1);
-      }
-      store(s0, 0);                                   // last one or two chunks: no loads
-      __syncthreads();
-      compute(0);
-      if (c + 1 < nchunks) {
-        store(s1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(lds);
         __syncthreads();
-        compute(1);
       }
 
       // ---- epilogue: lane holds rows 16m + 4*lg + i, column ln of each n-subtile ----
@@ -429,50 +430,24 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Args p) {
           const int fl = m_flat[w][r];
           if (fl < 0) continue;                         // padding row
           if constexpr (STAGE == STAGE_GATEUP) {
-            const int f = n0 + wave * 16 + ln;
-            const float g = acc[m][0][i], u = acc[m][1][i];
-            p.h[(int64_t)(row0 + r) * p.N + f] = silu(g) * u;
-          } else if (p.out_mode == GG_OUT_ATOMIC) {
-            const float wt = m_w[w][r];
-            float* orow = p.out + (int64_t)m_tok[w][r] * p.N + n0 + ln;
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-              __hip_atomic_fetch_add(orow + wrow[s], wt * acc[m][s][i], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+            for (int s = 0; s < 2; ++s) {
+              const int64_t o = (int64_t)(row0 + r) * p.N + n0 + wave * 32 + s * 16 + ln;
+              const float hv = silu(acc[m][s][i]) * acc[m][s + 2][i];
+              const _Float16 hh = (_Float16)hv;
+              p.ohi[o] = hh;
+              if constexpr (SPLIT) p.olo[o] = (_Float16)(hv - (float)hh);
+            }
           } else {
             float* yrow = p.y + (int64_t)fl * p.N + n0 + ln;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) yrow[wrow[s]] = acc[m][s][i];
+            for (int s = 0; s < 4; ++s) yrow[wrow[s]] = acc[m][s][i];
           }
         }
       }
-      __syncthreads();                                  // LDS buffers are reused by the next tile
+      __syncthreads();                                  // metadata / buffers reused next
     }
   }
-}
-
-// out[i] = residual ? residual[i] : 0 (start value of the atomic combine)
-__global__ __launch_bounds__(256) void init_out_kernel(float* __restrict__ out,
-                                                       const float* __restrict__ residual,
-                                                       int64_t n4) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  ((float4*)out)[i] = residual ? ((const float4*)residual)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-// Compute units of the current device (cached per device).
-static int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  if (cache[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      return -1;
-    cache[dev] = cus;
-  }
-  return cache[dev];
 }
 
 template <int FMT, int STAGE, int MSUB, bool SPLIT>
@@ -482,7 +457,7 @@ static hipError_t launch_t(const Args& a, int64_t R, hipStream_t s) {
   int64_t grid = max_m * a.n_tiles;                // upper bound of the tile count
   const int cus = device_cus();
   if (cus <= 0) return hipErrorInvalidDevice;
-  if (grid > cus) grid = cus;                       // persistent: one workgroup per CU
+  if (grid > (int64_t)cus * WG_PER_CU) grid = (int64_t)cus * WG_PER_CU;   // persistent
   hipLaunchKernelGGL((grouped_gemm_kernel<FMT, STAGE, MSUB, SPLIT>), dim3((unsigned)grid), dim3(NT),
                      0, s, a);
   return hipGetLastError();
@@ -498,7 +473,8 @@ static hipError_t launch_f(const Args& a, int64_t R, bool small_m, bool split, h
 }  // namespace gg
 
 bool grouped_supported(const ExpertsDev& W, bool need_gate_up) {
-  // down tiles are 256 columns of d_model; K chunks are 128 values
+  // down tiles are 256 columns of d_model, gate/up tiles 128 columns of d_ff; K is
+  // consumed in pairs of 64-value chunks
   if (W.D % 256 || W.F % 128) return false;
   if (W.fmt != MOE_FMT_Q8_0 && W.fmt != MOE_FMT_Q4) return false;
   auto a8 = [](const void* p) { return ((uintptr_t)p & 7) == 0; };
@@ -510,12 +486,14 @@ bool grouped_supported(const ExpertsDev& W, bool need_gate_up) {
 
 bool grouped_small_m(int64_t R) { return R <= 2048; }
 
-hipError_t launch_grouped_gateup(const float* a, int a_mode, const ExpertsDev& W,
-                                 const int32_t* offsets, const int32_t* rows, int64_t R, int k,
-                                 float* h_sorted, bool split, hipStream_t s) {
+hipError_t launch_grouped_gateup(const _Float16* xhi, const _Float16* xlo, int a_mode,
+                                 const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
+                                 int64_t R, int k, _Float16* hhi, _Float16* hlo, bool split,
+                                 hipStream_t s) {
   if (R <= 0) return hipSuccess;
   gg::Args p{};
-  p.a = a;
+  p.ahi = xhi;
+  p.alo = xlo;
   p.rows = rows;
   p.offsets = offsets;
   p.k = k;
@@ -529,23 +507,23 @@ hipError_t launch_grouped_gateup(const float* a, int a_mode, const ExpertsDev& W
   p.N = W.F;
   p.K = W.D;
   p.n_tiles = W.F / (gg::BN / 2);   // 128 columns of h per tile
-  p.out_mode = GG_OUT_H;
-  p.h = h_sorted;
+  p.ohi = hhi;
+  p.olo = hlo;
   const bool sm = grouped_small_m(R);
   return W.fmt == MOE_FMT_Q8_0
              ? gg::launch_f<MOE_FMT_Q8_0, gg::STAGE_GATEUP>(p, R, sm, split, s)
              : gg::launch_f<MOE_FMT_Q4, gg::STAGE_GATEUP>(p, R, sm, split, s);
 }
 
-hipError_t launch_grouped_down(const float* a, int a_mode, const ExpertsDev& W,
-                               const int32_t* offsets, const int32_t* rows, const float* topk_w,
-                               int64_t R, int k, float* out, float* y, bool split, hipStream_t s) {
+hipError_t launch_grouped_down(const _Float16* hhi, const _Float16* hlo, int a_mode,
+                               const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
+                               int64_t R, int k, float* y, bool split, hipStream_t s) {
   if (R <= 0) return hipSuccess;
   gg::Args p{};
-  p.a = a;
+  p.ahi = hhi;
+  p.alo = hlo;
   p.rows = rows;
   p.offsets = offsets;
-  p.topk_w = topk_w;
   p.k = k;
   p.a_mode = a_mode;
   p.w0 = W.down;
@@ -555,19 +533,36 @@ hipError_t launch_grouped_down(const float* a, int a_mode, const ExpertsDev& W,
   p.N = W.D;
   p.K = W.F;
   p.n_tiles = W.D / gg::BN;
-  p.out_mode = out ? GG_OUT_ATOMIC : GG_OUT_Y;
-  p.out = out;
   p.y = y;
   const bool sm = grouped_small_m(R);
   return W.fmt == MOE_FMT_Q8_0 ? gg::launch_f<MOE_FMT_Q8_0, gg::STAGE_DOWN>(p, R, sm, split, s)
                                : gg::launch_f<MOE_FMT_Q4, gg::STAGE_DOWN>(p, R, sm, split, s);
 }
 
-hipError_t launch_init_out(float* out, const float* residual, int64_t n, hipStream_t s) {
+// hi = fp16(v), lo = fp16(v - hi) for n values (n % 4 == 0, 16-byte aligned)
+__global__ __launch_bounds__(256) void to_planes_kernel(const float* __restrict__ src, int64_t n4,
+                                                        _Float16* __restrict__ hi,
+                                                        _Float16* __restrict__ lo) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = ((const float4*)src)[i];
+  const float a[4] = {v.x, v.y, v.z, v.w};
+  gg::h4 h, l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = (_Float16)a[j];
+    l[j] = (_Float16)(a[j] - (float)h[j]);
+  }
+  ((gg::h4*)hi)[i] = h;
+  if (lo) ((gg::h4*)lo)[i] = l;
+}
+
+hipError_t launch_to_planes(const float* src, int64_t n, _Float16* hi, _Float16* lo,
+                            hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t n4 = n / 4;
-  hipLaunchKernelGGL(gg::init_out_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, out,
-                     residual, n4);
+  hipLaunchKernelGGL(to_planes_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, src, n4,
+                     hi, lo);
   return hipGetLastError();
 }
 

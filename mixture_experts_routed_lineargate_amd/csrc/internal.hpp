@@ -104,6 +104,7 @@ struct Workspace {
   float* h;             // [T*k][F]
   float* y;             // [T*k][D]
   float* xn;            // [T][D]  normalised input (PRENORM)
+  _Float16* xp;         // [2][T][D] fp16 planes of the layer input (grouped kernels)
   uint32_t* sync;       // barrier / work-list words
   size_t bytes;
 };
@@ -133,15 +134,16 @@ hipError_t launch_rmsnorm(const float* x, int64_t T, int D, float eps, float* ou
 // grouped GEMM on MFMA (batched / prefill expert FFN)
 enum { GG_A_TOKEN = 0, GG_A_FLAT = 1, GG_A_SORTED = 2 };   // activation row of sorted row i:
                                                           // x[rows[i]/k], h[rows[i]], h[i]
-enum { GG_OUT_H = 0, GG_OUT_ATOMIC = 1, GG_OUT_Y = 2 };
 bool grouped_supported(const ExpertsDev& W, bool need_gate_up);
-hipError_t launch_grouped_gateup(const float* a, int a_mode, const ExpertsDev& W,
-                                 const int32_t* offsets, const int32_t* rows, int64_t R, int k,
-                                 float* h_sorted, bool split, hipStream_t s);
-hipError_t launch_grouped_down(const float* a, int a_mode, const ExpertsDev& W,
-                               const int32_t* offsets, const int32_t* rows, const float* topk_w,
-                               int64_t R, int k, float* out, float* y, bool split, hipStream_t s);
-hipError_t launch_init_out(float* out, const float* residual, int64_t n, hipStream_t s);
+hipError_t launch_grouped_gateup(const _Float16* xhi, const _Float16* xlo, int a_mode,
+                                 const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
+                                 int64_t R, int k, _Float16* hhi, _Float16* hlo, bool split,
+                                 hipStream_t s);
+hipError_t launch_grouped_down(const _Float16* hhi, const _Float16* hlo, int a_mode,
+                               const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
+                               int64_t R, int k, float* y, bool split, hipStream_t s);
+hipError_t launch_to_planes(const float* src, int64_t n, _Float16* hi, _Float16* lo,
+                            hipStream_t s);
 
 // fused single-token decode layer (D 2048, F 768, E 128, k 8)
 bool decode_fused_supported(const ExpertsDev& W, int64_t T, int k, const float* x);
