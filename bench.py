@@ -4,12 +4,14 @@
 Headline workload (the JSON line's ``value``): single-token decode through
 Qwen3-MoE-geometry MoE layers (d_model 2048, d_ff 768, 128 Q8_0 experts,
 Zipf-biased LinearGate, top-8).  One step = one token through 48 distinct layers
-chained with residual + RMSNorm (48 moe_layer calls, captured once as a HIP
-graph and replayed), so consecutive layer calls never reuse expert weights and
-the 256 MB Infinity Cache cannot serve them.  ``value`` = routed MoE-layer
-tokens/s = 48 * steps / elapsed.
+chained with residual + RMSNorm: one moe_decode_stack call (two persistent
+launches of 24 layers), captured once as a HIP graph and replayed.  Consecutive
+layers never reuse expert weights, so the 256 MB Infinity Cache cannot serve
+them.  ``value`` = routed MoE-layer tokens/s = 48 * steps / elapsed.
 
 The same run also measures, under ``workloads``:
+  decode_per_layer  the same 48-layer step as 48 moe_layer calls (one fused
+                 launch per layer)
   decode_batch   32 tokens x 16 chained 4-bit layers (residual + RMSNorm)
   prefill_down   the down projection + combine operator: 1024 tokens routed
                  top-8 (8192 rows of 768 fp32 activations), 4-bit W_down,
@@ -48,8 +50,11 @@ Q4_DOWN = 884_736                        # one 4-bit W_down: 2048 * 768 / 32 * 1
 GATE_BYTES = D * E * 4 + E * 4           # router matrix + bias
 DECODE_ALGO_BYTES = K * Q8_BLOB + GATE_BYTES + 2 * D * 4   # = 41,173,504
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-DECODE_SRC = os.path.join(ROOT, "mixture_experts_routed_lineargate_amd", "csrc", "decode.hip")
-WORKLOADS = ("decode_batch", "prefill_down", "prefill_stack")
+CSRC = os.path.join(ROOT, "mixture_experts_routed_lineargate_amd", "csrc")
+DECODE_SRC = os.path.join(CSRC, "decode.hip")
+STACK_SRCS = (os.path.join(CSRC, "decode_stack.hip"), os.path.join(CSRC, "decode_common.hpp"))
+STACK_LAYERS_PER_LAUNCH = 24
+WORKLOADS = ("decode_per_layer", "decode_batch", "prefill_down", "prefill_stack")
 
 
 def parse():
@@ -65,21 +70,34 @@ def parse():
     return ap.parse_args()
 
 
-def source_sha(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def counter_traffic(kernel_tag: str, src: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the source."""
-    p = os.path.join(PROFILE_DIR, f"{kernel_tag}_traffic.json")
+def counter_traffic(kernel_tag: str, srcs):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (``source_sha256:`` and
+    ``traffic_bytes_per_launch:`` lines of profiles/<kernel_tag>_traffic.md)."""
+    p = os.path.join(PROFILE_DIR, f"{kernel_tag}_traffic.md")
     if not os.path.exists(p):
         return None
+    fields = {}
     with open(p) as f:
-        t = json.load(f)
-    if t.get("source_sha256") != source_sha(src):
+        for line in f:
+            if ":" in line and line.split(":", 1)[0].strip() in ("source_sha256",
+                                                                 "traffic_bytes_per_launch"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != source_sha(srcs):
         return None
-    return t.get("traffic_bytes_per_launch")
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(arena, layers_np, budget_s: float):
@@ -279,25 +297,29 @@ def main():
     experts = [M.Experts.from_blobs(arena[l], D, F, S.FMT_Q8_0) for l in range(L)]
     flags = M.F_RESIDUAL | M.F_PRENORM
     ws = M.workspace(1, D, F, E, K, S.FMT_Q8_0, flags)
-    bufs = [torch.from_numpy(S.hidden(2, 1, D)).to(dev)] + \
-           [torch.empty((1, D), dtype=torch.float32, device=dev) for _ in range(L)]
+    x0 = torch.from_numpy(S.hidden(2, 1, D)).to(dev)
     stream = torch.cuda.Stream()
+    want = [w for w in a.workloads.split(",") if w]
 
-    def one_pass():
-        for l in range(L):
-            M.moe_layer(bufs[l], gates[l][0], gates[l][1], experts[l], K, bufs[l + 1],
-                        flags=flags if l > 0 else M.F_RESIDUAL, ws=ws, stream=stream)
+    # headline: one moe_decode_stack call per step
+    stack_layers = M.StackLayers([g for g, _ in gates], [b for _, b in gates], experts)
+    outs = torch.empty((L, D), dtype=torch.float32, device=dev)
 
-    ms_step = graph_time_ms(torch, one_pass, stream, a.warmup, a.steps)
+    def one_stack():
+        M.moe_decode_stack(x0[0], stack_layers, K, outs, ws=ws, stream=stream)
+
+    ms_step = graph_time_ms(torch, one_stack, stream, a.warmup, a.steps)
     err = int(ws[64:68].view(torch.int32).item())    # exchange-wait timeout flag
     if err:
         raise RuntimeError("decode kernel reported an exchange-wait timeout")
-    if not torch.isfinite(bufs[L]).all():
+    if not torch.isfinite(outs).all():
         raise RuntimeError("non-finite output")
-    print(f"[bench] decode: {ms_step * 1e3 / L:.2f} us per layer call", file=sys.stderr, flush=True)
+    print(f"[bench] decode stack: {ms_step * 1e3 / L:.2f} us per layer", file=sys.stderr, flush=True)
 
-    launch_s = ms_step / 1e3 / L                    # average fused-layer launch, events on its stream
-    achieved = DECODE_ALGO_BYTES / launch_s / 1e9
+    launches = -(-L // STACK_LAYERS_PER_LAUNCH)
+    launch_s = ms_step / 1e3 / launches             # average persistent launch, events on its stream
+    bytes_per_launch = DECODE_ALGO_BYTES * L / launches
+    achieved = bytes_per_launch / launch_s / 1e9
     value = L / (ms_step / 1e3)
     line = {
         "metric": "routed MoE-layer tokens/s",
@@ -318,18 +340,40 @@ def main():
                         "residual + RMSNorm per step",
             "tokens_per_layer_call": 1, "layers_per_step": L, "weights": "Q8_0",
             "algorithmic_bytes_per_layer_call": DECODE_ALGO_BYTES,
+            "launches_per_step": launches,
         },
         "hbm_gbps": round(achieved, 1),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": counter_traffic("decode_layer_q8_0", DECODE_SRC),
-            "kernel": "decode_layer_kernel<Q8_0>",
+            "traffic": counter_traffic("decode_stack_q8_0", STACK_SRCS),
+            "kernel": "decode_stack_kernel<Q8_0>",
             "avg_launch_us": round(launch_s * 1e6, 3),
+            "algorithmic_bytes_per_launch": int(bytes_per_launch),
         },
     }
-    want = [w for w in a.workloads.split(",") if w]
     extra = {}
+    if "decode_per_layer" in want:
+        bufs = [x0] + [torch.empty((1, D), dtype=torch.float32, device=dev) for _ in range(L)]
+
+        def one_pass():
+            for l in range(L):
+                M.moe_layer(bufs[l], gates[l][0], gates[l][1], experts[l], K, bufs[l + 1],
+                            flags=flags if l > 0 else M.F_RESIDUAL, ws=ws, stream=stream)
+
+        ms_pl = graph_time_ms(torch, one_pass, stream, a.warmup, a.steps)
+        if int(ws[64:68].view(torch.int32).item()):
+            raise RuntimeError("decode kernel reported an exchange-wait timeout")
+        diff = float((bufs[L][0] - outs[L - 1]).abs().max() / outs[L - 1].pow(2).mean().sqrt())
+        extra["decode_per_layer"] = {
+            "workload": "the same 48-layer step as 48 moe_layer calls (decode_layer_kernel<Q8_0>)",
+            "tokens_per_s": round(L / (ms_pl / 1e3), 1),
+            "us_per_layer": round(ms_pl * 1e3 / L, 3),
+            "hbm_gbps": round(DECODE_ALGO_BYTES / (ms_pl / 1e3 / L) / 1e9, 1),
+            "max_rel_diff_vs_stack": diff,
+        }
+        print(f"[bench] decode per layer: {ms_pl * 1e3 / L:.2f} us per layer call",
+              file=sys.stderr, flush=True)
     iters = max(3, min(20, a.steps // 10))
     if "decode_batch" in want:
         extra["decode_batch"], _ = bench_decode_batch(torch, M, S, dev, stream, iters)

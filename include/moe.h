@@ -178,6 +178,37 @@ moe_status moe_layer(const float* x, const float* gate, const float* bias,
                      float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
                      int32_t* sorted_rows, void* ws, size_t ws_bytes, void* stream);
 
+/* One layer of a decode stack (host struct holding device pointers). */
+typedef struct {
+  const float* gate;   /* [D][E] fp32 LinearGate matrix */
+  const float* bias;   /* [E] fp32 logit bias, or NULL */
+  moe_experts experts; /* the layer's experts */
+} moe_stack_layer;
+
+/* Single-token decode through num_layers consecutive MoE layers, each with its
+ * residual add, and the RMSNorm transition between layers (evidence page:
+ * "RMSNorm and residual transitions"; technical-overview page, warm target
+ * path ... router -> resident expert -> combine -> next layer):
+ *   in_0 = x, or x / sqrt(mean(x^2) + 1e-6) with MOE_F_PRENORM (for a stack
+ *   that continues an earlier one, x being its last output);
+ *   o_l = in_l + MoE_l(in_l);  in_{l+1} = o_l / sqrt(mean(o_l^2) + 1e-6).
+ * The whole stack is enqueued with no host synchronisation; on the tuned
+ * geometry (D 2048, F 768, E 128, k 8, every layer in one format, 16-byte
+ * aligned weight bases and strides) one persistent launch runs up to 24
+ * layers with no launch between them, and its fp outputs are
+ * bit-reproducible.  Other shapes run moe_layer per layer.
+ *   x [D] fp32 (one token); layers: host array of num_layers >= 1 entries;
+ *   outs [num_layers][D] fp32: o_l of every layer;
+ *   topk_ids [num_layers][k] int32, topk_w [num_layers][k] fp32: optional
+ *   (NULL) routing of every layer, as moe_route reports it.
+ *   flags: MOE_F_PRENORM or 0 (MOE_F_RESIDUAL and MOE_F_DETERMINISTIC are
+ *   implied and accepted).  ws: moe_workspace_bytes(1, D, F, E, k, format,
+ *   MOE_F_PRENORM) bytes, zero-filled before first use like every workspace. */
+moe_status moe_decode_stack(const float* x, int32_t num_layers,
+                            const moe_stack_layer* layers /* host */, int32_t k, int32_t flags,
+                            float* outs, int32_t* topk_ids, float* topk_w, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* RMSNorm with unit gain (evidence page: "RMSNorm and residual transitions"):
  * out[t] = x[t] / sqrt(mean_D(x[t]^2) + eps).  out may equal x. */
 moe_status moe_rmsnorm(const float* x, int64_t T, int32_t D, float eps, float* out, void* stream);

@@ -36,6 +36,10 @@ class moe_experts(ctypes.Structure):
     ]
 
 
+class moe_stack_layer(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("experts", moe_experts)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I32, _I64, _SZ, _F32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -51,6 +55,8 @@ _SIGS = {
     "moe_layer": (_I32, [_P, _P, _P, ctypes.POINTER(moe_experts), _I64, _I32, _I32, _P, _P, _P,
                          _P, _P, _P, _SZ, _P]),
     "moe_rmsnorm": (_I32, [_P, _I64, _I32, _F32, _P, _P]),
+    "moe_decode_stack": (_I32, [_P, _I32, ctypes.POINTER(moe_stack_layer), _I32, _I32, _P, _P,
+                                _P, _P, _SZ, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -215,3 +221,37 @@ def moe_rmsnorm(x, out, eps: float = 1e-6, stream=None):
     _need(out, torch.float32, "out")
     T, D = x.shape
     _check("moe_rmsnorm", lib().moe_rmsnorm(_ptr(x), T, D, eps, _ptr(out), _stream(stream)))
+
+
+class StackLayers:
+    """Host array of moe_stack_layer entries for moe_decode_stack (keeps the
+    tensors it points at alive)."""
+
+    def __init__(self, gates, biases, experts):
+        import torch
+        if not (len(gates) == len(biases) == len(experts)) or not gates:
+            raise ValueError("gates, biases and experts need one entry per layer")
+        for g, b in zip(gates, biases):
+            _need(g, torch.float32, "gate")
+            _need(b, torch.float32, "bias")
+        self.keep = (list(gates), list(biases), list(experts))
+        self.n = len(gates)
+        self.c = (moe_stack_layer * self.n)()
+        for i, (g, b, ex) in enumerate(zip(gates, biases, experts)):
+            self.c[i] = moe_stack_layer(_ptr(g), _ptr(b), ex.c)
+
+
+def moe_decode_stack(x, layers: StackLayers, k: int, outs, flags: int = 0, topk_ids=None,
+                     topk_w=None, ws=None, stream=None):
+    """Single-token decode through ``layers.n`` layers: outs [L][D] gets o_l."""
+    import torch
+    for t, dt, n in ((x, torch.float32, "x"), (outs, torch.float32, "outs"),
+                     (topk_ids, torch.int32, "topk_ids"), (topk_w, torch.float32, "topk_w"),
+                     (ws, torch.uint8, "ws")):
+        _need(t, dt, n)
+    if outs.shape[0] != layers.n or (topk_ids is not None and topk_ids.shape != (layers.n, k)) or (
+            topk_w is not None and topk_w.shape != (layers.n, k)):
+        raise ValueError("outs / topk_ids / topk_w need one row per layer")
+    _check("moe_decode_stack", lib().moe_decode_stack(
+        _ptr(x), layers.n, layers.c, k, flags, _ptr(outs), _ptr(topk_ids), _ptr(topk_w),
+        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))

@@ -148,6 +148,36 @@ static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const 
   return MOE_OK;
 }
 
+// The body of moe_layer after validation.
+static moe_status layer_impl(const float* x, const float* gate, const float* bias,
+                             const moe_experts* W, int64_t T, int k, int flags, float* out,
+                             int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                             int32_t* sorted_rows, void* ws, hipStream_t s) {
+  const int D = W->d_model, F = W->d_ff, E = W->num_experts;
+  const Workspace w = carve_workspace(ws, T, D, F, E, k, flags);
+  const ExpertsDev dev = to_dev(*W);
+  int32_t* ids = topk_ids ? topk_ids : w.ids;
+  float* wts = topk_w ? topk_w : w.w;
+  int32_t* offs = expert_offsets ? expert_offsets : w.offsets;
+  int32_t* rows = sorted_rows ? sorted_rows : w.rows;
+  if (decode_fused_supported(dev, T, k, x)) {
+    trace("layer fused decode", T, D, F, E, k, W->format);
+    HIP_TRY(launch_decode_fused(x, gate, bias, dev, out, topk_ids, topk_w, expert_offsets,
+                                sorted_rows, flags, w, s));
+    return MOE_OK;
+  }
+  trace("layer generic", T, D, F, E, k, W->format);
+  const float* u = x;
+  if (flags & MOE_F_PRENORM) {
+    HIP_TRY(launch_rmsnorm(x, T, D, PRENORM_EPS, w.xn, s));
+    u = w.xn;
+  }
+  MOE_TRY(do_route(u, T, D, gate, bias, E, k, ids, wts, w, s));
+  HIP_TRY(launch_group(ids, T * k, E, offs, rows, s));
+  return do_ffn(u, MOE_STAGE_FULL, dev, ids, wts, offs, rows, T, k, nullptr, out,
+                flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC | MOE_F_FP16_ACT), w, s);
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -266,29 +296,74 @@ moe_status moe_layer(const float* x, const float* gate, const float* bias, const
     return MOE_E_ALIGN;
   const size_t need = moe_workspace_bytes(T, D, F, E, k, W->format, flags);
   if (!ws || ws_bytes < need) return MOE_E_WORKSPACE;
-  const Workspace w = carve_workspace(ws, T, D, F, E, k, flags);
+  return layer_impl(x, gate, bias, W, T, k, flags, out, topk_ids, topk_w, expert_offsets,
+                    sorted_rows, ws, (hipStream_t)stream);
+}
+
+moe_status moe_decode_stack(const float* x, int32_t num_layers, const moe_stack_layer* layers,
+                            int32_t k, int32_t flags, float* outs, int32_t* topk_ids,
+                            float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  if (num_layers <= 0) return MOE_E_SHAPE;
+  if (!layers || !x || !outs) return MOE_E_NULLPTR;
+  if (flags & ~(MOE_F_PRENORM | MOE_F_RESIDUAL | MOE_F_DETERMINISTIC)) return MOE_E_FORMAT;
+  const moe_experts* W0 = &layers[0].experts;
+  for (int l = 0; l < num_layers; ++l) {
+    const moe_experts* W = &layers[l].experts;
+    MOE_TRY(check_experts(W));
+    MOE_TRY(check_gate_up(W));
+    if (W->d_model != W0->d_model || W->d_ff != W0->d_ff || W->num_experts != W0->num_experts)
+      return MOE_E_SHAPE;
+    if (!layers[l].gate) return MOE_E_NULLPTR;
+    if (!aligned(layers[l].gate, 4) || (layers[l].bias && !aligned(layers[l].bias, 4)))
+      return MOE_E_ALIGN;
+  }
+  const int D = W0->d_model, F = W0->d_ff, E = W0->num_experts;
+  MOE_TRY(check_dims(1, D, E, k));
+  if (!aligned(x, 4) || !aligned(outs, 4) || (topk_ids && !aligned(topk_ids, 4)) ||
+      (topk_w && !aligned(topk_w, 4)))
+    return MOE_E_ALIGN;
+  size_t need = 0;
+  for (int l = 0; l < num_layers; ++l) {
+    const size_t n = moe_workspace_bytes(1, D, F, E, k, layers[l].experts.format,
+                                         MOE_F_PRENORM | MOE_F_RESIDUAL);
+    need = n > need ? n : need;
+  }
+  if (!ws || ws_bytes < need) return MOE_E_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  const ExpertsDev dev = to_dev(*W);
-  int32_t* ids = topk_ids ? topk_ids : w.ids;
-  float* wts = topk_w ? topk_w : w.w;
-  int32_t* offs = expert_offsets ? expert_offsets : w.offsets;
-  int32_t* rows = sorted_rows ? sorted_rows : w.rows;
-  if (decode_fused_supported(dev, T, k, x)) {
-    trace("layer fused decode", T, D, F, E, k, W->format);
-    HIP_TRY(launch_decode_fused(x, gate, bias, dev, out, topk_ids, topk_w, expert_offsets,
-                                sorted_rows, flags, w, s));
+  const Workspace w = carve_workspace(ws, 1, D, F, E, k, MOE_F_PRENORM | MOE_F_RESIDUAL);
+
+  bool fused = aligned(x, 16) && aligned(outs, 16);
+  for (int l = 0; l < num_layers && fused; ++l) {
+    const ExpertsDev dv = to_dev(layers[l].experts);
+    fused = decode_fused_supported(dv, 1, k, x) && dv.fmt == W0->format;
+  }
+  fused = fused && decode_stack_supported(W0->format);
+  const int LM = decode_stack_max_layers();
+  if (fused) {
+    trace("decode stack fused", 1, D, F, E, k, W0->format);
+    StackLayer sl[64];
+    for (int c = 0; c < num_layers; c += LM) {
+      const int n = num_layers - c < LM ? num_layers - c : LM;
+      for (int i = 0; i < n; ++i)
+        sl[i] = StackLayer{layers[c + i].gate, layers[c + i].bias, to_dev(layers[c + i].experts)};
+      const float* in = c == 0 ? x : outs + (size_t)(c - 1) * D;
+      const bool pre = c > 0 || (flags & MOE_F_PRENORM);
+      HIP_TRY(launch_decode_stack(in, n, sl, W0->format, pre, outs + (size_t)c * D,
+                                  topk_ids ? topk_ids + (size_t)c * k : nullptr,
+                                  topk_w ? topk_w + (size_t)c * k : nullptr, w, s));
+    }
     return MOE_OK;
   }
-  trace("layer generic", T, D, F, E, k, W->format);
-  const float* u = x;
-  if (flags & MOE_F_PRENORM) {
-    HIP_TRY(launch_rmsnorm(x, T, D, PRENORM_EPS, w.xn, s));
-    u = w.xn;
+  trace("decode stack per layer", 1, D, F, E, k, W0->format);
+  for (int l = 0; l < num_layers; ++l) {
+    const float* in = l == 0 ? x : outs + (size_t)(l - 1) * D;
+    const int fl = MOE_F_RESIDUAL | MOE_F_DETERMINISTIC |
+                   ((l > 0 || (flags & MOE_F_PRENORM)) ? MOE_F_PRENORM : 0);
+    MOE_TRY(layer_impl(in, layers[l].gate, layers[l].bias, &layers[l].experts, 1, k, fl,
+                       outs + (size_t)l * D, topk_ids ? topk_ids + (size_t)l * k : nullptr,
+                       topk_w ? topk_w + (size_t)l * k : nullptr, nullptr, nullptr, ws, s));
   }
-  MOE_TRY(do_route(u, T, D, gate, bias, E, k, ids, wts, w, s));
-  HIP_TRY(launch_group(ids, T * k, E, offs, rows, s));
-  return do_ffn(u, MOE_STAGE_FULL, dev, ids, wts, offs, rows, T, k, nullptr, out,
-                flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC | MOE_F_FP16_ACT), w, s);
+  return MOE_OK;
 }
 
 moe_status moe_rmsnorm(const float* x, int64_t T, int32_t D, float eps, float* out, void* stream) {

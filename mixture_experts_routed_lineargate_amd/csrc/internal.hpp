@@ -111,7 +111,7 @@ struct Workspace {
 
 int router_ksplit(int64_t T, int D);
 Workspace carve_workspace(void* base, int64_t T, int D, int F, int E, int k, int flags);
-constexpr size_t SYNC_BYTES = 1024 * 1024;  // barrier words and exchange buffers
+constexpr size_t SYNC_BYTES = 2 * 1024 * 1024;  // barrier words and exchange buffers
 
 bool trace_enabled();
 void trace(const char* what, int64_t T, int D, int F, int E, int k, int fmt);
@@ -151,5 +151,17 @@ hipError_t launch_decode_fused(const float* x, const float* gate, const float* b
                                const ExpertsDev& W, float* out, int32_t* ids, float* w,
                                int32_t* offsets, int32_t* rows, int flags, const Workspace& ws,
                                hipStream_t s);
+
+// single-token decode through a stack of layers in one launch (same geometry)
+struct StackLayer {
+  const float* gate;
+  const float* bias;
+  ExpertsDev W;
+};
+int decode_stack_max_layers();
+bool decode_stack_supported(int fmt);
+hipError_t launch_decode_stack(const float* x, int L, const StackLayer* layers, int fmt,
+                               bool prenorm0, float* outs, int32_t* ids, float* w,
+                               const Workspace& ws, hipStream_t s);
 
 }  // namespace moe

@@ -128,3 +128,30 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(M, "LIB_PATH", "/nonexistent/libmoe_mi355x.so")
     with pytest.raises(RuntimeError, match="missing"):
         M.lib()
+
+
+def test_decode_stack_validation():
+    L = M.lib()
+    ex = _experts()
+
+    def layers(*exs, gate=FAKE):
+        return (M.moe_stack_layer * len(exs))(*[M.moe_stack_layer(gate, None, e) for e in exs])
+
+    two = layers(ex, ex)
+
+    def call(n=2, lay=two, k=8, flags=0, x=FAKE, outs=FAKE, ws=FAKE, wsb=1 << 40):
+        return L.moe_decode_stack(x, n, lay, k, flags, outs, None, None, ws, wsb, None)
+
+    assert call(n=0) == 2
+    assert call(lay=None) == 1
+    assert call(x=None) == 1
+    assert call(outs=None) == 1
+    assert call(flags=M.F_FP16_ACT) == 4
+    assert call(k=0) == 2
+    assert call(k=33) == 6
+    assert call(x=FAKE + 2) == 3
+    assert call(ws=None) == 5
+    assert call(wsb=1000) == 5
+    assert call(lay=layers(ex, _experts(d_ff=1536))) == 2
+    assert call(lay=layers(ex, _experts(format=3))) == 4
+    assert call(n=1, lay=layers(ex, gate=None)) == 1

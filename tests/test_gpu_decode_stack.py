@@ -1,0 +1,106 @@
+"""GPU parity of the single-token decode stack (moe_decode_stack).
+
+One token runs through a stack of Qwen3-MoE-geometry layers (d_model 2048, d_ff
+768, 128 experts, Zipf-biased LinearGate routers, top-8), each with its residual
+add, and the RMSNorm transition between layers.  The GPU runs free on its own
+trajectory (one persistent launch per 24 layers); at every layer its o_l and
+expert ids are compared with the oracle's trajectory.  Tokens are taken from
+seeded candidates whose fp64 trajectory keeps the 8th/9th router-logit gap at or
+above 1e-3 at every layer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import cases
+import mixture_experts_routed_lineargate_amd as M
+import moe_synth as S
+from oracle import moe_oracle as O
+from pins import rel_max_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+D, F, E, K = 2048, 768, 128, 8
+TOL = 2e-3
+
+
+def pick_tokens(cfg, L, fmt, arena, gates, n_cand, n_keep, prenorm, seed):
+    cand = S.hidden(cfg, n_cand, D, layer=seed)
+    if prenorm:
+        cand = cand * np.float32(3.0)
+    x0 = O.rmsnorm(cand) if prenorm else cand
+    ref = cases.stack_oracle(x0, gates, arena, D, F, K, fmt)
+    gap = np.min([O.topk_gap(r["logits"], K) for r in ref], axis=0)
+    keep = np.nonzero(gap >= cases.GAP)[0][:n_keep]
+    assert keep.size >= 1, "no candidate keeps the gap rule through the stack"
+    print(f"\ndecode stack: tokens {keep.tolist()} of {n_cand} keep the gap "
+          f"(min gaps {gap[keep].tolist()})", flush=True)
+    return cand, ref, keep
+
+
+def run_stack(x, dG, ex, flags, ws):
+    L = len(dG)
+    layers = M.StackLayers([g for g, _ in dG], [b for _, b in dG], ex)
+    outs = torch.full((L, D), float("nan"), dtype=torch.float32, device=DEV)
+    ids = torch.full((L, K), -1, dtype=torch.int32, device=DEV)
+    w = torch.zeros((L, K), dtype=torch.float32, device=DEV)
+    M.moe_decode_stack(torch.from_numpy(x).to(DEV), layers, K, outs, flags=flags, topk_ids=ids,
+                       topk_w=w, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws[64:68].view(torch.int32).item()) == 0, "exchange-wait timeout"
+    return outs.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+def check_trajectory(ref, t, outs, ids, w):
+    worst = 0.0
+    for l, r in enumerate(ref):
+        assert np.array_equal(ids[l], r["ids"][t]), f"layer {l}: expert ids differ"
+        assert np.abs(w[l] - r["w"][t]).max() <= 1e-5, f"layer {l}: routing weights"
+        err = rel_max_err(outs[l][None], r["out"][t][None])
+        worst = max(worst, err)
+        assert err <= TOL, f"layer {l}: max|d|/rms = {err:.3e}"
+    return worst
+
+
+def test_decode_stack_48_layers_q8_0():
+    L = 48
+    arena = S.device_arena(2, L, E, D, F, S.FMT_Q8_0, DEV)
+    gates = cases.stack_layers(2, L, E, D, K)
+    cand, ref, keep = pick_tokens(2, L, S.FMT_Q8_0, arena, gates, 4, 2, False, 600)
+    dG = [(torch.from_numpy(G).to(DEV), torch.from_numpy(b).to(DEV)) for G, b in gates]
+    ex = [M.Experts.from_blobs(arena[l], D, F, S.FMT_Q8_0) for l in range(L)]
+    ws = M.workspace(1, D, F, E, K, S.FMT_Q8_0, M.F_PRENORM)
+    first = None
+    for t in keep:
+        outs, ids, w = run_stack(cand[t], dG, ex, 0, ws)
+        worst = check_trajectory(ref, t, outs, ids, w)
+        print(f"decode stack Q8_0: token {t}: worst per-layer max|d|/rms = {worst:.2e}", flush=True)
+        if first is None:
+            first = (t, outs)
+    # the single-layer kernel on the same workspace in between, then the stack again:
+    # launch counters stay in step and the result is bit-identical
+    t0, outs0 = first
+    out1 = torch.empty((1, D), dtype=torch.float32, device=DEV)
+    M.moe_layer(torch.from_numpy(cand[t0][None]).to(DEV), dG[0][0], dG[0][1], ex[0], K, out1,
+                flags=M.F_RESIDUAL, ws=ws)
+    again, _, _ = run_stack(cand[t0], dG, ex, 0, ws)
+    assert np.array_equal(again.view(np.uint32), outs0.view(np.uint32)), "not bit-reproducible"
+    del arena
+    torch.cuda.empty_cache()
+
+
+def test_decode_stack_q4_prenorm_crosses_launches():
+    """30 4-bit layers: two launches (24 + 6); the first layer normalises its input."""
+    L = 30
+    arena = S.device_arena(3, L, E, D, F, S.FMT_Q4, DEV)
+    gates = cases.stack_layers(3, L, E, D, K)
+    cand, ref, keep = pick_tokens(3, L, S.FMT_Q4, arena, gates, 3, 1, True, 700)
+    dG = [(torch.from_numpy(G).to(DEV), torch.from_numpy(b).to(DEV)) for G, b in gates]
+    ex = [M.Experts.from_blobs(arena[l], D, F, S.FMT_Q4) for l in range(L)]
+    ws = M.workspace(1, D, F, E, K, S.FMT_Q4, M.F_PRENORM)
+    t = keep[0]
+    outs, ids, w = run_stack(cand[t], dG, ex, M.F_PRENORM, ws)
+    worst = check_trajectory(ref, t, outs, ids, w)
+    print(f"decode stack Q4: token {t}: worst per-layer max|d|/rms = {worst:.2e}", flush=True)
+    del arena
+    torch.cuda.empty_cache()
