@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--workloads", default=",".join(WORKLOADS),
                     help="comma list of extra workloads to measure (empty for none)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters in a profiler run)")
     return ap.parse_args()
 
 
@@ -300,6 +303,14 @@ def main():
     x0 = torch.from_numpy(S.hidden(2, 1, D)).to(dev)
     stream = torch.cuda.Stream()
     want = [w for w in a.workloads.split(",") if w]
+    if a.calib_copy_mib:
+        n = a.calib_copy_mib << 18                    # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # headline: one moe_decode_stack call per step
     stack_layers = M.StackLayers([g for g, _ in gates], [b for _, b in gates], experts)
