@@ -108,10 +108,12 @@ static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const 
   auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
   if (grouped_supported(W, full) && a16(in) && a16(y) && a16(out)) {
     const bool split = !(flags & MOE_F_FP16_ACT);
+    const bool skinny = skinny_supported(W, R, full);
     trace(full ? (split ? "ffn grouped mfma gate/up+down (split fp16)"
                         : "ffn grouped mfma gate/up+down (fp16)")
                : (split ? "ffn grouped mfma down (split fp16)" : "ffn grouped mfma down (fp16)"),
           T, W.D, W.F, W.E, k, W.fmt);
+    if (skinny) trace("  (weight-slice kernels: few rows per expert)", T, W.D, W.F, W.E, k, W.fmt);
     // activations as fp16 planes (hi, lo): x [T][D] in ws.xp, h [R][F] in the h region
     _Float16* hhi = (_Float16*)ws.h;
     _Float16* hlo = split ? hhi + (size_t)R * W.F : nullptr;
@@ -120,15 +122,22 @@ static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const 
       _Float16* xhi = ws.xp;
       _Float16* xlo = split ? xhi + (size_t)T * W.D : nullptr;
       HIP_TRY(launch_to_planes(in, T * (int64_t)W.D, xhi, xlo, s));
-      HIP_TRY(launch_grouped_gateup(xhi, xlo, GG_A_TOKEN, W, offsets, rows, R, k, hhi, hlo, split,
-                                    s));
+      if (skinny)
+        HIP_TRY(launch_skinny_gateup(xhi, xlo, GG_A_TOKEN, W, offsets, rows, R, k, hhi, hlo, split,
+                                     s));
+      else
+        HIP_TRY(launch_grouped_gateup(xhi, xlo, GG_A_TOKEN, W, offsets, rows, R, k, hhi, hlo,
+                                      split, s));
       a_mode = GG_A_SORTED;
     } else {
       HIP_TRY(launch_to_planes(in, R * (int64_t)W.F, hhi, hlo, s));
     }
     const float* res = (full && (flags & MOE_F_RESIDUAL)) ? in : nullptr;
     float* ybuf = y ? y : ws.y;
-    HIP_TRY(launch_grouped_down(hhi, hlo, a_mode, W, offsets, rows, R, k, ybuf, split, s));
+    if (skinny)
+      HIP_TRY(launch_skinny_down(hhi, hlo, a_mode, W, offsets, rows, R, k, ybuf, split, s));
+    else
+      HIP_TRY(launch_grouped_down(hhi, hlo, a_mode, W, offsets, rows, R, k, ybuf, split, s));
     if (out) HIP_TRY(launch_combine(ybuf, w, T, k, W.D, res, out, s));
     return MOE_OK;
   }

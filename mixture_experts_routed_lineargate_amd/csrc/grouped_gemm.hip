@@ -36,15 +36,10 @@
 // 16-byte pieces XOR-swizzled by row (conflict-free fragment reads), weight rows
 // transposed into dword slabs (thread t loads row t; padded slab stride keeps the
 // four lane groups of a fragment in distinct banks).
-#include "internal.hpp"
+#include "mfma_frag.hpp"
 
 namespace moe {
 namespace gg {
-
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;               // threads per workgroup (4 wavefronts, two workgroups per CU)
 constexpr int NW = NT / WAVE;
@@ -99,57 +94,6 @@ __device__ inline int xcd_swizzle(int bid, int total) {
 template <int FMT>
 __device__ inline uint32_t wdw(const uint32_t* col, int off) { return col[(off >> 2) * Fmt<FMT>::SLAB]; }
 
-// The 8 weights k = 8g .. 8g+7 of block b as exact fp16 (q, or q - 8).
-template <int FMT>
-__device__ inline h8 block_frag(const uint32_t* col, int b, int g) {
-  constexpr int BB = Fmt<FMT>::BB;
-  union {
-    uint32_t u[4];
-    h2 p[4];
-    h8 v;
-  } r;
-  if constexpr (FMT == MOE_FMT_Q8_0) {
-    const int s = b * BB + 2 + 8 * g;                  // 2 mod 4 when b is even
-    uint32_t q0, q1;
-    if (s & 2) {
-      const uint32_t d0 = wdw<FMT>(col, s - 2), d1 = wdw<FMT>(col, s + 2), d2 = wdw<FMT>(col, s + 6);
-      q0 = __builtin_amdgcn_alignbyte(d1, d0, 2);
-      q1 = __builtin_amdgcn_alignbyte(d2, d1, 2);
-    } else {
-      q0 = wdw<FMT>(col, s);
-      q1 = wdw<FMT>(col, s + 4);
-    }
-    // two's complement -> biased unsigned, then 0x64uu = 1024 + u as fp16
-    q0 ^= 0x80808080u;
-    q1 ^= 0x80808080u;
-    r.u[0] = __builtin_amdgcn_perm(0x64646464u, q0, 0x04010400u);
-    r.u[1] = __builtin_amdgcn_perm(0x64646464u, q0, 0x04030402u);
-    r.u[2] = __builtin_amdgcn_perm(0x64646464u, q1, 0x04010400u);
-    r.u[3] = __builtin_amdgcn_perm(0x64646464u, q1, 0x04030402u);
-    const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};   // 1024 + 128
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.p[i] = r.p[i] - bias;
-  } else {
-    const int s = b * BB + 2 + 4 * g;                  // 2 mod 4 when b is even
-    uint32_t n;
-    if (s & 2) {
-      n = __builtin_amdgcn_alignbyte(wdw<FMT>(col, s + 2), wdw<FMT>(col, s - 2), 2);
-    } else {
-      n = wdw<FMT>(col, s);
-    }
-    // byte j holds element 2j (low nibble) and 2j+1 (high nibble)
-    const uint32_t lo = n & 0x0f0f0f0fu, hi = (n >> 4) & 0x0f0f0f0fu;
-    r.u[0] = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x64006400u;
-    r.u[1] = __builtin_amdgcn_perm(hi, lo, 0x0c050c01u) | 0x64006400u;
-    r.u[2] = __builtin_amdgcn_perm(hi, lo, 0x0c060c02u) | 0x64006400u;
-    r.u[3] = __builtin_amdgcn_perm(hi, lo, 0x0c070c03u) | 0x64006400u;
-    const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};   // 1024 + 8
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.p[i] = r.p[i] - bias;
-  }
-  return r.v;
-}
-
 // Compute units of the current device (cached per device).
 static int device_cus() {
   static int cache[64];
@@ -165,20 +109,10 @@ static int device_cus() {
   return cache[dev];
 }
 
-// Block b's 8 weights k = 8g .. 8g+7 as an exact pair of fp16 vectors: d*q = hi + lo
-// with hi = fp16(d*q) and lo = d*q - hi (d*q has at most 19 significant bits, so lo
-// is exact; needs |d*q| < 65504, i.e. |d| < 511 for Q8_0 and |d| < 8187 for 4-bit).
+// Block b's weights as an exact fp16 pair, from a row in the slab layout.
 template <int FMT>
 __device__ inline void block_frag_hl(const uint32_t* col, int b, int g, h8& hi, h8& lo) {
-  const h8 q = block_frag<FMT>(col, b, g);
-  constexpr int BB = Fmt<FMT>::BB;
-  const int ob = b * BB;
-  const uint32_t w = wdw<FMT>(col, ob & ~3);
-  const uint16_t bits = (ob & 2) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
-  const _Float16 d = __builtin_bit_cast(_Float16, bits);
-  const h8 dd = {d, d, d, d, d, d, d, d};
-  hi = q * dd;
-  lo = __builtin_elementwise_fma(q, dd, -hi);
+  frag_hl<FMT>([=](int off) { return wdw<FMT>(col, off); }, b, g, hi, lo);
 }
 
 // Persistent: each workgroup walks tiles L = slot, slot + G, ... where slot()

@@ -144,6 +144,15 @@ hipError_t launch_grouped_down(const _Float16* hhi, const _Float16* hlo, int a_m
                                int64_t R, int k, float* y, bool split, hipStream_t s);
 hipError_t launch_to_planes(const float* src, int64_t n, _Float16* hi, _Float16* lo,
                             hipStream_t s);
+// few rows per expert (R <= 512) at the tuned geometry: weight-slice kernels, same operands
+bool skinny_supported(const ExpertsDev& W, int64_t R, bool need_gate_up);
+hipError_t launch_skinny_gateup(const _Float16* xhi, const _Float16* xlo, int a_mode,
+                                const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
+                                int64_t R, int k, _Float16* hhi, _Float16* hlo, bool split,
+                                hipStream_t s);
+hipError_t launch_skinny_down(const _Float16* hhi, const _Float16* hlo, int a_mode,
+                              const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
+                              int64_t R, int k, float* y, bool split, hipStream_t s);
 
 // fused single-token decode layer (D 2048, F 768, E 128, k 8)
 bool decode_fused_supported(const ExpertsDev& W, int64_t T, int k, const float* x);

@@ -12,6 +12,7 @@ namespace moe {
 int router_ksplit(int64_t T, int D) {
   const int64_t tiles = T >= 32 ? (T + 31) / 32 : (T + 7) / 8;
   int64_t ks = 256 / (tiles > 0 ? tiles : 1);
+  if (ks > 16) ks = 16;            // the top-k pass sums ks partials per logit
   if (ks < 1) ks = 1;
   if (ks > D / 32) ks = D / 32;
   int dchunk = (int)(((D + ks - 1) / ks + 31) / 32 * 32);
@@ -81,25 +82,46 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restri
                                                            float* __restrict__ part) {
   __shared__ float xs[RT_K][RT_T + 4];        // [k][token], padded
   __shared__ __attribute__((aligned(16))) float gs[RT_K][RT_E];
+  constexpr int XL = RT_T * RT_K / 256, GL = RT_K * RT_E / 256;   // loads per thread per chunk
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * RT_T;
   const int sl = blockIdx.y;
   const int d0 = sl * dchunk, d1 = min(D, d0 + dchunk);
   const int tg = tid / 32, eg = tid % 32;     // tokens 4*tg.., experts 4*eg..
   float acc[4][4] = {};
+  // A chunk's loads are all issued before any is used (clamped addresses, values
+  // masked afterwards), and the next chunk's are in flight during this chunk's FMAs.
+  float xr[XL], gr[GL];
+  auto load = [&](int dd) {
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int i = j * 256 + tid, tt = i / RT_K, c = i % RT_K;
+      const int64_t t = min(t0 + tt, T - 1);
+      xr[j] = x[t * D + min(dd + c, D - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < GL; ++j) {
+      const int i = j * 256 + tid, c = i / RT_E, e = i % RT_E;
+      gr[j] = G[(int64_t)min(dd + c, D - 1) * E + min(e, E - 1)];
+    }
+  };
+  auto store = [&](int dd) {
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int i = j * 256 + tid, tt = i / RT_K, c = i % RT_K;
+      xs[c][tt] = (t0 + tt < T && dd + c < d1) ? xr[j] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < GL; ++j) {
+      const int i = j * 256 + tid, c = i / RT_E, e = i % RT_E;
+      gs[c][e] = (e < E && dd + c < d1) ? gr[j] : 0.f;
+    }
+  };
+  load(d0);
   for (int dd = d0; dd < d1; dd += RT_K) {
-    // x chunk: 32 tokens x 32 d (one float per thread-pair step), stored transposed
-    for (int i = tid; i < RT_T * RT_K; i += 256) {
-      const int tt = i / RT_K, c = i % RT_K;
-      const int64_t t = t0 + tt;
-      xs[c][tt] = (t < T && dd + c < d1) ? x[t * D + dd + c] : 0.f;
-    }
-    // G chunk: 32 d x 128 experts
-    for (int i = tid; i < RT_K * RT_E; i += 256) {
-      const int c = i / RT_E, e = i % RT_E;
-      gs[c][e] = (e < E && dd + c < d1) ? G[(int64_t)(dd + c) * E + e] : 0.f;
-    }
+    store(dd);
     __syncthreads();
+    if (dd + RT_K < d1) load(dd + RT_K);
 #pragma unroll 8
     for (int c = 0; c < RT_K; ++c) {
       const float4 xv = *(const float4*)&xs[c][4 * tg];
@@ -140,12 +162,13 @@ hipError_t launch_router_partial(const float* x, int64_t T, int D, const float* 
 // One wavefront per token: sum the D-slice partials (fixed order), add the
 // bias, pick k winners by (value desc, index asc), then weights
 // w_j = exp(l_j - l_max) / sum_selected exp(l - l_max), written in ascending id order.
+// PL = logits per lane (E <= 64 * PL).
+template <int PL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ part, int ksplit,
                                                    int64_t T, int E,
                                                    const float* __restrict__ bias, int k,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
-  constexpr int PL = MAX_E / WAVE;  // logits per lane
   __shared__ float sel_l[4][MAX_K];
   __shared__ int sel_e[4][MAX_K];
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
@@ -157,8 +180,19 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
     const int e = i * WAVE + lane;
     float s = -FLT_MAX;
     if (e < E) {
+      // 16 partials in flight at a time, summed in slice order
       s = 0.f;
-      for (int p = 0; p < ksplit; ++p) s += part[((int64_t)p * T + t) * E + e];
+      for (int p0 = 0; p0 < ksplit; p0 += 16) {
+        float pv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int p = min(p0 + j, ksplit - 1);
+          pv[j] = part[((int64_t)p * T + t) * E + e];
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (p0 + j < ksplit) s += pv[j];
+      }
       if (bias) s += bias[e];
     }
     v[i] = s;
@@ -202,8 +236,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
 
 hipError_t launch_topk(const float* part, int ksplit, int64_t T, int E, const float* bias, int k,
                        int32_t* ids, float* w, hipStream_t s) {
+  static_assert(MAX_E <= 16 * WAVE, "logits per lane");
   dim3 grid((unsigned)((T + 3) / 4));
-  hipLaunchKernelGGL(topk_kernel, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w);
+  if (E <= WAVE)
+    hipLaunchKernelGGL(topk_kernel<1>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w);
+  else if (E <= 2 * WAVE)
+    hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w);
+  else if (E <= 4 * WAVE)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w);
+  else
+    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w);
   return hipGetLastError();
 }
 

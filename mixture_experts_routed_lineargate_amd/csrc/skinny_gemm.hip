@@ -1,0 +1,349 @@
+// Expert FFN on MFMA for few routed rows per expert (a decode batch: 32 tokens
+// x top-8 over 128 experts gives ~7 rows per active expert).  Same two stages
+// and the same operands as the grouped GEMM (grouped_gemm.hip): activations as
+// fp16 planes, weights as exact fp16 pairs (mfma_frag.hpp), fp32 accumulation.
+//
+// With so few rows the grouped GEMM's tiles (256 weight rows, a K loop of
+// 64-value chunks two deep) are few and latency-bound.  Here the weight slice
+// is the unit of work: a workgroup owns one active expert and a slice of its
+// weight rows (gate/up: 16 gate + 16 up rows = 16 columns of h; down: 64 rows),
+// loads the whole slice (K = 2048 or 768) into LDS at once, and applies it to
+// every row routed to that expert, 32 rows per pass.  The four wavefronts split
+// K into quarters and add their partial tiles in LDS in wavefront order, so the
+// result does not depend on timing.  Weight rows sit in LDS with a stride that
+// is an odd multiple of 16 bytes, which puts the 16 rows x 4 lane groups of a
+// fragment read in distinct banks.  The grid is persistent: every workgroup
+// compacts the list of experts with rows from expert_offsets (in LDS) and walks
+// the (active expert, slice) items with a stride of the grid size.
+#include "mfma_frag.hpp"
+
+namespace moe {
+namespace sk {
+
+using gg::h8;
+constexpr int NT = 256;       // 4 wavefronts
+constexpr int NW = NT / WAVE;
+constexpr int MROWS = 32;     // rows per pass (two 16-row M-tiles)
+constexpr int PD = 4;         // activation-fragment prefetch depth (blocks)
+constexpr int D_TUNED = 2048, F_TUNED = 768;
+constexpr int E_MAX = 256;    // experts per layer this kernel takes
+enum { STAGE_GATEUP = 0, STAGE_DOWN = 1 };
+
+__host__ __device__ constexpr int padded_row(int rb) { return ((rb / 16) % 2 == 0) ? rb + 16 : rb; }
+
+template <int FMT, int STAGE>
+struct Geo {
+  static constexpr int BB = FMT == MOE_FMT_Q8_0 ? 34 : 18;
+  static constexpr int K = STAGE == STAGE_GATEUP ? D_TUNED : F_TUNED;
+  static constexpr int N = STAGE == STAGE_GATEUP ? F_TUNED : D_TUNED;   // output columns
+  static constexpr int RB = K / QK * BB;          // bytes per stored weight row
+  static constexpr int RBP = padded_row(RB);      // LDS row stride
+  static constexpr int WR = STAGE == STAGE_GATEUP ? 32 : 64;   // weight rows per workgroup
+  static constexpr int NS = WR / 16;              // 16-row n-subtiles
+  static constexpr int COLS = STAGE == STAGE_GATEUP ? 16 : 64; // output columns per workgroup
+  static constexpr int NCB = N / COLS;            // workgroups per expert
+  static constexpr int CHUNKS = WR * RB / 16;     // 16-byte pieces of the slice
+  static constexpr int LPT = (CHUNKS + NT - 1) / NT;   // pieces per thread
+  static constexpr int BPW = K / QK / NW;         // blocks per wavefront
+  static constexpr int W_BYTES = WR * RBP;
+  static constexpr int RED_BYTES = (NW - 1) * 2 * NS * WAVE * 16;
+  static_assert(RB % 16 == 0 && (RBP / 16) % 2 == 1, "row stride");
+  static_assert(K % (QK * NW) == 0 && N % COLS == 0, "shape");
+  static_assert(BPW % PD == 0 || BPW >= PD, "prefetch ring");
+};
+
+struct Args {
+  const _Float16* ahi;
+  const _Float16* alo;
+  const int32_t* rows;
+  const int32_t* offsets;
+  int k;
+  int a_mode;                 // GG_A_*: activation row of sorted row i
+  const uint8_t* w0;          // gate (gate/up stage) or down
+  int64_t s0;
+  const uint8_t* w1;          // up
+  int64_t s1;
+  int E, R;
+  _Float16* ohi;              // gate/up: h planes [R][N] in sorted order
+  _Float16* olo;
+  float* y;                   // down: y [R][N] in flat order
+};
+
+// One pass over up to 32 rows (MT 16-row M-tiles) of the current item, for this
+// wavefront's quarter of K: the wavefront's partial tile goes to acc.
+template <int FMT, int STAGE, bool SPLIT, int MT>
+__device__ inline void pass_tiles(const Args& p, const uint8_t* wl, const int* m_src, int kb0,
+                                  int lane, f32x4 (&acc)[2][Geo<FMT, STAGE>::NS]) {
+  using G = Geo<FMT, STAGE>;
+  constexpr int PL = SPLIT ? 2 : 1;
+  constexpr int PDM = MT == 1 ? 2 * PD : PD;        // deeper prefetch when one M-tile
+  const int ln = lane % 16, lg = lane / 16;
+  int64_t arow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) arow[m] = (int64_t)m_src[16 * m + ln] * G::K;
+  h8 ra[PDM][MT][PL];                               // prefetch ring of activation fragments
+  auto aload = [&](int j, int slot) {
+    const int o = (kb0 + j) * QK + 8 * lg;
+#pragma unroll
+    for (int pl = 0; pl < PL; ++pl) {
+      const _Float16* a = pl ? p.alo : p.ahi;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) ra[slot][m][pl] = *(const h8*)(a + arow[m] + o);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < PDM; ++j)
+    if (j < G::BPW) aload(j, j);
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int s = 0; s < G::NS; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < G::BPW; ++j) {
+    const int b = kb0 + j, slot = j % PDM;
+    h8 bh[G::NS], bl[G::NS];
+#pragma unroll
+    for (int s = 0; s < G::NS; ++s) {
+      const uint32_t* rw = (const uint32_t*)(wl + (16 * s + ln) * G::RBP);
+      gg::frag_hl<FMT>([=](int off) { return rw[off >> 2]; }, b, lg, bh[s], bl[s]);
+    }
+    h8 ah[MT], al[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      ah[m] = ra[slot][m][0];
+      if constexpr (SPLIT) al[m] = ra[slot][m][1];
+    }
+    if (j + PDM < G::BPW) aload(j + PDM, slot);
+    // acc += a_hi (w_hi + w_lo) [+ a_lo w_hi]; the dropped a_lo w_lo is below 2^-22
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int s = 0; s < G::NS; ++s) {
+        acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bh[s], acc[m][s], 0, 0, 0);
+        acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bl[s], acc[m][s], 0, 0, 0);
+        if constexpr (SPLIT)
+          acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[m], bh[s], acc[m][s], 0, 0, 0);
+      }
+  }
+}
+
+template <int FMT, int STAGE, bool SPLIT>
+__global__ __launch_bounds__(NT) void skinny_kernel(Args p) {
+  using G = Geo<FMT, STAGE>;
+  __shared__ __attribute__((aligned(16))) uint8_t wl[G::W_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t red[G::RED_BYTES];
+  __shared__ int m_src[MROWS];
+  __shared__ int m_flat[MROWS];
+  __shared__ int act[E_MAX];                        // experts with rows, ascending
+  __shared__ int aoff[2 * E_MAX];                   // their clamped row ranges (lo, hi)
+  __shared__ int n_act;
+
+  const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+  const int ln = lane % 16, lg = lane / 16;
+
+  // ---- active experts (wavefront 0, in expert order) ----
+  if (wave == 0) {
+    int base = 0;
+    for (int e0 = 0; e0 < p.E; e0 += WAVE) {
+      const int e = e0 + lane;
+      int lo = 0, hi = 0;
+      if (e < p.E) {
+        lo = min(max(p.offsets[e], 0), p.R);
+        hi = min(max(p.offsets[e + 1], lo), p.R);
+      }
+      const bool on = e < p.E && hi > lo;
+      const uint64_t m = __ballot(on);
+      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+      if (on) {
+        act[pos] = e;
+        aoff[2 * pos] = lo;
+        aoff[2 * pos + 1] = hi;
+      }
+      base += __popcll(m);
+    }
+    if (lane == 0) n_act = base;
+  }
+  __syncthreads();
+  const int items = n_act * G::NCB;
+  const int kb0 = wave * G::BPW;                    // this wavefront's first block
+
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int u = it / G::NCB, cb = it % G::NCB;
+    const int e = act[u], r0 = aoff[2 * u], r1 = aoff[2 * u + 1], re = r1 - r0;
+
+    // ---- the weight slice, all of it in flight at once ----
+    const int n0 = cb * (STAGE == STAGE_GATEUP ? 16 : G::COLS);
+    u32x4 wv[G::LPT];
+#pragma unroll
+    for (int i = 0; i < G::LPT; ++i) {
+      const int c = min(i * NT + tid, G::CHUNKS - 1);   // clamped: unconditional loads
+      const int row = c / (G::RB / 16), col = c % (G::RB / 16);
+      const uint8_t* src;
+      if constexpr (STAGE == STAGE_GATEUP)
+        src = row < 16 ? p.w0 + (int64_t)e * p.s0 + (int64_t)(n0 + row) * G::RB
+                       : p.w1 + (int64_t)e * p.s1 + (int64_t)(n0 + row - 16) * G::RB;
+      else
+        src = p.w0 + (int64_t)e * p.s0 + (int64_t)(n0 + row) * G::RB;
+      wv[i] = __builtin_nontemporal_load((const u32x4*)(src + 16 * col));
+    }
+#pragma unroll
+    for (int i = 0; i < G::LPT; ++i) {
+      const int c = i * NT + tid;
+      if (c < G::CHUNKS) {
+        const int row = c / (G::RB / 16), col = c % (G::RB / 16);
+        *(u32x4*)(wl + row * G::RBP + 16 * col) = wv[i];
+      }
+    }
+
+    for (int pass = 0; pass * MROWS < re; ++pass) {
+      if (tid < MROWS) {
+        const int i = r0 + pass * MROWS + tid;
+        int src = 0, fl = -1;
+        if (i < r1) {
+          const int f = p.rows[i];
+          if ((unsigned)f < (unsigned)p.R) {
+            fl = f;
+            src = p.a_mode == GG_A_TOKEN ? f / p.k : (p.a_mode == GG_A_FLAT ? f : i);
+          }
+        }
+        m_src[tid] = src;
+        m_flat[tid] = fl;
+      }
+      __syncthreads();                                // weights (first pass) and row metadata
+      f32x4 acc[2][G::NS];
+      if (re - pass * MROWS <= 16)
+        pass_tiles<FMT, STAGE, SPLIT, 1>(p, wl, m_src, kb0, lane, acc);
+      else
+        pass_tiles<FMT, STAGE, SPLIT, 2>(p, wl, m_src, kb0, lane, acc);
+      const int mt = re - pass * MROWS <= 16 ? 1 : 2;
+
+      // ---- K quarters summed in wavefront order, epilogue by wavefront 0 ----
+      f32x4* rd = (f32x4*)red;
+      if (wave > 0) {
+        for (int m = 0; m < mt; ++m)
+#pragma unroll
+          for (int s = 0; s < G::NS; ++s) rd[(((wave - 1) * 2 + m) * G::NS + s) * WAVE + lane] = acc[m][s];
+      }
+      __syncthreads();
+      if (wave == 0) {
+        for (int m = 0; m < mt; ++m) {
+#pragma unroll
+          for (int w = 1; w < NW; ++w)
+#pragma unroll
+            for (int s = 0; s < G::NS; ++s) acc[m][s] += rd[(((w - 1) * 2 + m) * G::NS + s) * WAVE + lane];
+          // lane holds rows 16m + 4*lg + i, column ln of each n-subtile
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * m + 4 * lg + i;
+            const int fl = m_flat[r];
+            if (fl < 0) continue;                     // padding row
+            if constexpr (STAGE == STAGE_GATEUP) {
+              const int64_t o = (int64_t)(r0 + pass * MROWS + r) * G::N + n0 + ln;
+              const float hv = silu(acc[m][0][i]) * acc[m][1][i];
+              const _Float16 hh = (_Float16)hv;
+              p.ohi[o] = hh;
+              if constexpr (SPLIT) p.olo[o] = (_Float16)(hv - (float)hh);
+            } else {
+              float* yrow = p.y + (int64_t)fl * G::N + n0 + ln;
+#pragma unroll
+              for (int s = 0; s < G::NS; ++s) yrow[16 * s] = acc[m][s][i];
+            }
+          }
+        }
+      }
+      __syncthreads();                                // metadata, partials and weights reused
+    }
+  }
+}
+
+// Resident workgroups of a kernel on the current device (cached), 0 on failure.
+template <typename Kern>
+static int resident(Kern k, int slot) {
+  static int cache[64][8];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || slot < 0 || slot >= 8) return 0;
+  if (cache[dev][slot] == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, NT, 0) != hipSuccess || per <= 0)
+      return 0;
+    cache[dev][slot] = cus * per;
+  }
+  return cache[dev][slot];
+}
+
+template <int FMT, int STAGE, bool SPLIT>
+static hipError_t launch_t(const Args& a, hipStream_t s) {
+  using G = Geo<FMT, STAGE>;
+  auto k = skinny_kernel<FMT, STAGE, SPLIT>;
+  const int slot = FMT * 4 + STAGE * 2 + (SPLIT ? 1 : 0);
+  int grid = resident(k, slot);
+  if (grid <= 0) return hipErrorInvalidDevice;
+  const int items = a.E * G::NCB;                   // upper bound of the item count
+  if (grid > items) grid = items;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT, int STAGE>
+static hipError_t launch_f(const Args& a, bool split, hipStream_t s) {
+  return split ? launch_t<FMT, STAGE, true>(a, s) : launch_t<FMT, STAGE, false>(a, s);
+}
+
+}  // namespace sk
+
+bool skinny_supported(const ExpertsDev& W, int64_t R, bool need_gate_up) {
+  if (W.D != sk::D_TUNED || W.F != sk::F_TUNED || R > 512 || W.E > sk::E_MAX) return false;
+  if (W.fmt != MOE_FMT_Q8_0 && W.fmt != MOE_FMT_Q4) return false;
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (!a16(W.down) || (W.down_stride & 15)) return false;
+  if (need_gate_up && (!a16(W.gate) || !a16(W.up) || (W.gate_stride & 15) || (W.up_stride & 15)))
+    return false;
+  return true;
+}
+
+hipError_t launch_skinny_gateup(const _Float16* xhi, const _Float16* xlo, int a_mode,
+                                const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
+                                int64_t R, int k, _Float16* hhi, _Float16* hlo, bool split,
+                                hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  sk::Args p{};
+  p.ahi = xhi;
+  p.alo = xlo;
+  p.rows = rows;
+  p.offsets = offsets;
+  p.k = k;
+  p.a_mode = a_mode;
+  p.w0 = W.gate;
+  p.s0 = W.gate_stride;
+  p.w1 = W.up;
+  p.s1 = W.up_stride;
+  p.E = W.E;
+  p.R = (int)R;
+  p.ohi = hhi;
+  p.olo = hlo;
+  return W.fmt == MOE_FMT_Q8_0 ? sk::launch_f<MOE_FMT_Q8_0, sk::STAGE_GATEUP>(p, split, s)
+                               : sk::launch_f<MOE_FMT_Q4, sk::STAGE_GATEUP>(p, split, s);
+}
+
+hipError_t launch_skinny_down(const _Float16* hhi, const _Float16* hlo, int a_mode,
+                              const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
+                              int64_t R, int k, float* y, bool split, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  sk::Args p{};
+  p.ahi = hhi;
+  p.alo = hlo;
+  p.rows = rows;
+  p.offsets = offsets;
+  p.k = k;
+  p.a_mode = a_mode;
+  p.w0 = W.down;
+  p.s0 = W.down_stride;
+  p.E = W.E;
+  p.R = (int)R;
+  p.y = y;
+  return W.fmt == MOE_FMT_Q8_0 ? sk::launch_f<MOE_FMT_Q8_0, sk::STAGE_DOWN>(p, split, s)
+                               : sk::launch_f<MOE_FMT_Q4, sk::STAGE_DOWN>(p, split, s);
+}
+
+}  // namespace moe
