@@ -32,6 +32,8 @@ Workspace carve_workspace(void* base, int64_t T, int D, int F, int E, int k, int
   w.y = (float*)take(tk * (size_t)D * sizeof(float));
   w.xn = (flags & MOE_F_PRENORM) ? (float*)take((size_t)T * D * sizeof(float)) : nullptr;
   w.xp = (_Float16*)take((size_t)T * D * 2 * sizeof(_Float16));
+  w.ssq = (float*)take((size_t)ks * (size_t)T * sizeof(float));
+  w.inv = (float*)take((size_t)T * sizeof(float));
   w.bytes = off;
   return w;
 }
@@ -99,10 +101,13 @@ static moe_status do_route(const float* x, int64_t T, int D, const float* G, con
   return MOE_OK;
 }
 
+// planes_ready: the FULL stage's input planes are already in ws.xp (made by the
+// top-k pass); res_scale: the residual row t is in[t] * res_scale[t].
 static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const int32_t* ids,
                          const float* w, const int32_t* offsets, const int32_t* rows, int64_t T,
                          int k, float* y, float* out, int flags, const Workspace& ws,
-                         hipStream_t s) {
+                         hipStream_t s, bool planes_ready = false,
+                         const float* res_scale = nullptr) {
   const bool full = stage == MOE_STAGE_FULL;
   const int64_t R = T * k;
   auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
@@ -121,7 +126,7 @@ static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const 
     if (full) {
       _Float16* xhi = ws.xp;
       _Float16* xlo = split ? xhi + (size_t)T * W.D : nullptr;
-      HIP_TRY(launch_to_planes(in, T * (int64_t)W.D, xhi, xlo, s));
+      if (!planes_ready) HIP_TRY(launch_to_planes(in, T * (int64_t)W.D, xhi, xlo, s));
       if (skinny)
         HIP_TRY(launch_skinny_gateup(xhi, xlo, GG_A_TOKEN, W, offsets, rows, R, k, hhi, hlo, split,
                                      s));
@@ -138,7 +143,7 @@ static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const 
       HIP_TRY(launch_skinny_down(hhi, hlo, a_mode, W, offsets, rows, R, k, ybuf, split, s));
     else
       HIP_TRY(launch_grouped_down(hhi, hlo, a_mode, W, offsets, rows, R, k, ybuf, split, s));
-    if (out) HIP_TRY(launch_combine(ybuf, w, T, k, W.D, res, out, s));
+    if (out) HIP_TRY(launch_combine(ybuf, w, T, k, W.D, res, out, s, res_scale));
     return MOE_OK;
   }
   const char* path = full ? "ffn generic gate/up+down" : "ffn generic down";
@@ -174,6 +179,29 @@ static moe_status layer_impl(const float* x, const float* gate, const float* bia
     HIP_TRY(launch_decode_fused(x, gate, bias, dev, out, topk_ids, topk_w, expert_offsets,
                                 sorted_rows, flags, w, s));
     return MOE_OK;
+  }
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (grouped_supported(dev, true) && a16(x) && a16(out) && D % 4 == 0) {
+    // MFMA path: the router also sums x^2 per slice; the top-k pass forms the
+    // RMSNorm factor, the routing, and the fp16 planes of the normalised input, so
+    // neither a normalisation pass nor a separate conversion pass runs
+    trace("layer grouped (fused norm + planes)", T, D, F, E, k, W->format);
+    const bool pre = (flags & MOE_F_PRENORM) != 0;
+    const bool split = !(flags & MOE_F_FP16_ACT);
+    const int ks = router_ksplit(T, D);
+    HIP_TRY(launch_router_partial(x, T, D, gate, E, w.part_logits, ks, s, pre ? w.ssq : nullptr));
+    TopkExtra ex;
+    ex.ssq = pre ? w.ssq : nullptr;
+    ex.D = D;
+    ex.inv = pre ? w.inv : nullptr;
+    ex.x = x;
+    ex.xhi = w.xp;
+    ex.xlo = split ? w.xp + (size_t)T * D : nullptr;
+    HIP_TRY(launch_topk(w.part_logits, ks, T, E, bias, k, ids, wts, s, ex));
+    HIP_TRY(launch_group(ids, T * k, E, offs, rows, s));
+    return do_ffn(x, MOE_STAGE_FULL, dev, ids, wts, offs, rows, T, k, nullptr, out,
+                  flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC | MOE_F_FP16_ACT), w, s,
+                  /*planes_ready=*/true, pre ? w.inv : nullptr);
   }
   trace("layer generic", T, D, F, E, k, W->format);
   const float* u = x;

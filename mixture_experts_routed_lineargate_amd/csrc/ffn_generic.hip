@@ -117,6 +117,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const float* __restrict__ w, int64_t T,
                                                       int k, int D,
                                                       const float* __restrict__ residual,
+                                                      const float* __restrict__ res_scale,
                                                       float* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int d = (blockIdx.y * 256 + threadIdx.x) * V;
@@ -136,8 +137,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
   }
   if (residual) {
+    const float rs = res_scale ? res_scale[t] : 1.0f;   // residual = rs * residual row
 #pragma unroll
-    for (int i = 0; i < V; ++i) s[i] += residual[t * D + d + i];
+    for (int i = 0; i < V; ++i) s[i] += res_scale ? residual[t * D + d + i] * rs : residual[t * D + d + i];
   }
   if constexpr (V == 4)
     *(float4*)(out + t * D + d) = make_float4(s[0], s[1], s[2], s[3]);
@@ -146,14 +148,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int D,
-                          const float* residual, float* out, hipStream_t s) {
+                          const float* residual, float* out, hipStream_t s,
+                          const float* res_scale) {
   auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
   if (D % 4 == 0 && a16(y) && a16(out) && a16(residual)) {
     dim3 grid((unsigned)T, (unsigned)((D / 4 + 255) / 256));
-    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, s, y, w, T, k, D, residual, out);
+    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, s, y, w, T, k, D, residual, res_scale, out);
   } else {
     dim3 grid((unsigned)T, (unsigned)((D + 255) / 256));
-    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, s, y, w, T, k, D, residual, out);
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, s, y, w, T, k, D, residual, res_scale, out);
   }
   return hipGetLastError();
 }

@@ -124,12 +124,9 @@ __device__ inline void block_frag_hl(const uint32_t* col, int b, int g, h8& hi, 
 // into LDS in one batch, so the dependent index loads cost one round trip per
 // window rather than per tile.
 //
-// K pipeline: activations (fp16 planes) and raw weight blocks go from global
-// memory straight into one of two LDS buffers (global_load_lds), two chunks in
-// flight.  Every wavefront issues exactly the same number of loads per chunk,
-// so an explicit vmcnt wait names the chunk that must have landed; plain
-// s_barrier is used in the loop because __syncthreads would also wait for the
-// chunk still in flight.
+// K pipeline: see the loop below (two register stages, one LDS buffer, two
+// barriers per 64-value chunk; a second LDS buffer would cost the second
+// workgroup per CU).
 //
 // Wavefront w computes 64 rows x 64 weight rows (4 x 4 MFMA tiles): down rows
 // 64w .. 64w+63, or gate rows 32w .. 32w+31 (subtiles 0, 1) and the up rows

@@ -105,6 +105,8 @@ struct Workspace {
   float* y;             // [T*k][D]
   float* xn;            // [T][D]  normalised input (PRENORM)
   _Float16* xp;         // [2][T][D] fp16 planes of the layer input (grouped kernels)
+  float* ssq;           // [ksplit][T] per-slice sums of squares of the layer input
+  float* inv;           // [T] RMSNorm factors
   uint32_t* sync;       // barrier / work-list words
   size_t bytes;
 };
@@ -117,18 +119,32 @@ bool trace_enabled();
 void trace(const char* what, int64_t T, int D, int F, int E, int k, int fmt);
 
 // ---- launchers (return hipError_t of the launch) ----
+// ssq (optional, [ksplit][T]): each slice's per-token sum of x^2 as well
 hipError_t launch_router_partial(const float* x, int64_t T, int D, const float* G, int E,
-                                 float* part, int ksplit, hipStream_t s);
+                                 float* part, int ksplit, hipStream_t s, float* ssq = nullptr);
+// With ssq: inv_t = 1/sqrt(mean(x_t^2) + eps) scales the logits (the router is
+// linear in x) and goes to inv[t]; with xhi: the fp16 planes of u_t = inv_t x_t
+// (inv_t = 1 without ssq) go to xhi / xlo (xlo may be null).
+struct TopkExtra {
+  const float* ssq = nullptr;
+  int D = 0;
+  float* inv = nullptr;
+  const float* x = nullptr;
+  _Float16* xhi = nullptr;
+  _Float16* xlo = nullptr;
+};
 hipError_t launch_topk(const float* part, int ksplit, int64_t T, int E, const float* bias, int k,
-                       int32_t* ids, float* w, hipStream_t s);
+                       int32_t* ids, float* w, hipStream_t s, const TopkExtra& ex = TopkExtra());
 hipError_t launch_group(const int32_t* ids, int64_t N, int E, int32_t* offsets, int32_t* rows,
                         hipStream_t s);
 hipError_t launch_gateup_generic(const float* x, const ExpertsDev& W, const int32_t* ids, int64_t T,
                                  int k, float* h, hipStream_t s);
 hipError_t launch_down_generic(const float* h, const ExpertsDev& W, const int32_t* ids, int64_t T,
                                int k, float* y, hipStream_t s);
+// residual row t is scaled by res_scale[t] when res_scale is given
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int D,
-                          const float* residual, float* out, hipStream_t s);
+                          const float* residual, float* out, hipStream_t s,
+                          const float* res_scale = nullptr);
 hipError_t launch_rmsnorm(const float* x, int64_t T, int D, float eps, float* out, hipStream_t s);
 
 // grouped GEMM on MFMA (batched / prefill expert FFN)

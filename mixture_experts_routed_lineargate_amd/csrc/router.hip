@@ -12,7 +12,7 @@ namespace moe {
 int router_ksplit(int64_t T, int D) {
   const int64_t tiles = T >= 32 ? (T + 31) / 32 : (T + 7) / 8;
   int64_t ks = 256 / (tiles > 0 ? tiles : 1);
-  if (ks > 16) ks = 16;            // the top-k pass sums ks partials per logit
+  if (ks > 32) ks = 32;            // the top-k pass sums ks partials per logit
   if (ks < 1) ks = 1;
   if (ks > D / 32) ks = D / 32;
   int dchunk = (int)(((D + ks - 1) / ks + 31) / 32 * 32);
@@ -27,7 +27,8 @@ template <int TT>
 __global__ __launch_bounds__(256) void router_partial_kernel(const float* __restrict__ x, int64_t T,
                                                              int D, const float* __restrict__ G,
                                                              int E, int dchunk,
-                                                             float* __restrict__ part) {
+                                                             float* __restrict__ part,
+                                                             float* __restrict__ ssq) {
   constexpr int DC = 32;
   constexpr int TH = TT / 2;
   __shared__ float xs[TT][DC];
@@ -37,6 +38,9 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const float* __rest
   const int d0 = s * dchunk;
   const int d1 = min(D, d0 + dchunk);
   const int el = tid & 127, half = tid >> 7;
+  float sq[TH];                                   // sum of x^2 over the slice
+#pragma unroll
+  for (int i = 0; i < TH; ++i) sq[i] = 0.f;
   for (int ec = 0; ec < E; ec += 128) {
     const int e = ec + el;
     float acc[TH];
@@ -50,6 +54,11 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const float* __rest
         xs[tt][c] = (t < T) ? x[t * D + dd + c] : 0.f;
       }
       __syncthreads();
+      if (ec == 0) {
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+          for (int i = 0; i < TH; ++i) sq[i] = fmaf(xs[half * TH + i][c], xs[half * TH + i][c], sq[i]);
+      }
       if (e < E) {
 #pragma unroll 8
         for (int c = 0; c < DC; ++c) {
@@ -67,6 +76,13 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const float* __rest
       }
     }
   }
+  if (ssq && el == 0) {
+#pragma unroll
+    for (int i = 0; i < TH; ++i) {
+      const int64_t t = t0 + half * TH + i;
+      if (t < T) ssq[(int64_t)s * T + t] = sq[i];
+    }
+  }
 }
 
 // Register-tiled fp32 router GEMM for many tokens and E <= 128 experts:
@@ -79,7 +95,8 @@ constexpr int RT_T = 32, RT_E = 128, RT_K = 32;
 __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restrict__ x, int64_t T,
                                                            int D, const float* __restrict__ G,
                                                            int E, int dchunk,
-                                                           float* __restrict__ part) {
+                                                           float* __restrict__ part,
+                                                           float* __restrict__ ssq) {
   __shared__ float xs[RT_K][RT_T + 4];        // [k][token], padded
   __shared__ __attribute__((aligned(16))) float gs[RT_K][RT_E];
   constexpr int XL = RT_T * RT_K / 256, GL = RT_K * RT_E / 256;   // loads per thread per chunk
@@ -89,6 +106,7 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restri
   const int d0 = sl * dchunk, d1 = min(D, d0 + dchunk);
   const int tg = tid / 32, eg = tid % 32;     // tokens 4*tg.., experts 4*eg..
   float acc[4][4] = {};
+  float sq[4] = {};                           // sum of x^2 over the slice, tokens 4*tg..
   // A chunk's loads are all issued before any is used (clamped addresses, values
   // masked afterwards), and the next chunk's are in flight during this chunk's FMAs.
   float xr[XL], gr[GL];
@@ -128,11 +146,20 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restri
       const float4 gv = *(const float4*)&gs[c][4 * eg];
       const float xa[4] = {xv.x, xv.y, xv.z, xv.w}, ga[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        sq[i] = fmaf(xa[i], xa[i], sq[i]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], ga[j], acc[i][j]);
+      }
     }
     __syncthreads();
+  }
+  if (ssq && eg == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + 4 * tg + i;
+      if (t < T) ssq[(int64_t)sl * T + t] = sq[i];
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -147,20 +174,22 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restri
 }
 
 hipError_t launch_router_partial(const float* x, int64_t T, int D, const float* G, int E,
-                                 float* part, int ksplit, hipStream_t s) {
+                                 float* part, int ksplit, hipStream_t s, float* ssq) {
   const int dchunk = router_dchunk(D, ksplit);
   if (E <= RT_E && T >= RT_T) {
     dim3 grid((unsigned)((T + RT_T - 1) / RT_T), (unsigned)ksplit);
-    hipLaunchKernelGGL(router_tiled_kernel, grid, dim3(256), 0, s, x, T, D, G, E, dchunk, part);
+    hipLaunchKernelGGL(router_tiled_kernel, grid, dim3(256), 0, s, x, T, D, G, E, dchunk, part, ssq);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((T + 7) / 8), (unsigned)ksplit);
-  hipLaunchKernelGGL(router_partial_kernel<8>, grid, dim3(256), 0, s, x, T, D, G, E, dchunk, part);
+  hipLaunchKernelGGL(router_partial_kernel<8>, grid, dim3(256), 0, s, x, T, D, G, E, dchunk, part,
+                     ssq);
   return hipGetLastError();
 }
 
-// One wavefront per token: sum the D-slice partials (fixed order), add the
-// bias, pick k winners by (value desc, index asc), then weights
+// One wavefront per token: sum the D-slice partials (fixed order), scale by the
+// RMSNorm factor when the router saw the raw input, add the bias, pick k
+// winners by (value desc, index asc), then weights
 // w_j = exp(l_j - l_max) / sum_selected exp(l - l_max), written in ascending id order.
 // PL = logits per lane (E <= 64 * PL).
 template <int PL>
@@ -168,31 +197,75 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
                                                    int64_t T, int E,
                                                    const float* __restrict__ bias, int k,
                                                    int32_t* __restrict__ ids,
-                                                   float* __restrict__ w) {
+                                                   float* __restrict__ w, TopkExtra ex) {
   __shared__ float sel_l[4][MAX_K];
   __shared__ int sel_e[4][MAX_K];
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;  // whole wavefront leaves together; no block barrier below
+  // RMSNorm factor from the router's per-slice sums of squares (slice order)
+  float inv = 1.0f;
+  if (ex.ssq) {
+    float ss = 0.f;
+    for (int p0 = 0; p0 < ksplit; p0 += 32) {
+      float pv[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) pv[j] = ex.ssq[(int64_t)min(p0 + j, ksplit - 1) * T + t];
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (p0 + j < ksplit) ss += pv[j];
+    }
+    inv = 1.0f / sqrtf(ss / (float)ex.D + PRENORM_EPS);
+    if (ex.inv && lane == 0) ex.inv[t] = inv;
+  }
+  // fp16 planes of u = inv * x for the MFMA expert kernels (eight float4 loads per
+  // lane in flight at a time)
+  if (ex.xhi) {
+    const float* xr = ex.x + t * ex.D;
+    for (int d0 = 0; d0 < ex.D; d0 += 8 * 4 * WAVE) {
+      float4 q[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = *(const float4*)(xr + min(d0 + 4 * (j * WAVE + lane), ex.D - 4));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = d0 + 4 * (j * WAVE + lane);
+        if (d >= ex.D) break;
+        const float u[4] = {q[j].x * inv, q[j].y * inv, q[j].z * inv, q[j].w * inv};
+        _Float16 hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hi[i] = (_Float16)u[i];
+          lo[i] = (_Float16)(u[i] - (float)hi[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ex.xhi[t * ex.D + d + i] = hi[i];
+        if (ex.xlo) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ex.xlo[t * ex.D + d + i] = lo[i];
+        }
+      }
+    }
+  }
   float v[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
     const int e = i * WAVE + lane;
     float s = -FLT_MAX;
     if (e < E) {
-      // 16 partials in flight at a time, summed in slice order
+      // 32 partials in flight at a time, summed in slice order
       s = 0.f;
-      for (int p0 = 0; p0 < ksplit; p0 += 16) {
-        float pv[16];
+      for (int p0 = 0; p0 < ksplit; p0 += 32) {
+        float pv[32];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 32; ++j) {
           const int p = min(p0 + j, ksplit - 1);
           pv[j] = part[((int64_t)p * T + t) * E + e];
         }
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < 32; ++j)
           if (p0 + j < ksplit) s += pv[j];
       }
+      s *= inv;
       if (bias) s += bias[e];
     }
     v[i] = s;
@@ -235,17 +308,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
 }
 
 hipError_t launch_topk(const float* part, int ksplit, int64_t T, int E, const float* bias, int k,
-                       int32_t* ids, float* w, hipStream_t s) {
+                       int32_t* ids, float* w, hipStream_t s, const TopkExtra& ex) {
   static_assert(MAX_E <= 16 * WAVE, "logits per lane");
   dim3 grid((unsigned)((T + 3) / 4));
   if (E <= WAVE)
-    hipLaunchKernelGGL(topk_kernel<1>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w);
+    hipLaunchKernelGGL(topk_kernel<1>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w, ex);
   else if (E <= 2 * WAVE)
-    hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w);
+    hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w, ex);
   else if (E <= 4 * WAVE)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w);
+    hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w, ex);
   else
-    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w);
+    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, s, part, ksplit, T, E, bias, k, ids, w, ex);
   return hipGetLastError();
 }
 
