@@ -236,10 +236,6 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
     const float inv = s_inv;
     const int e_j = min(max(sel_e[slot], 0), E - 1);
     const float w_j = sel_w[slot];
-    if (wg == 0 && tid < K) {
-      if (p.ids) p.ids[l * K + tid] = sel_e[tid];
-      if (p.w) p.w[l * K + tid] = sel_w[tid];
-    }
     if (router && tid < SLICE) in_reg = o_reg * inv;
 
     // ---- W + H: stream the weight share two groups ahead of the gate/up dots ----
@@ -345,6 +341,12 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
       }
       acc = sum8(acc);
       if (sub == 0) publish(p.xd + slot * D + dr0 + row, t, w_j * acc);
+    }
+    // the routing record goes out last: a store waits for its completion at the
+    // next wait for a load, and here that is the next exchange
+    if (wg == 0 && tid < K) {
+      if (p.ids) p.ids[l * K + tid] = sel_e[tid];
+      if (p.w) p.w[l * K + tid] = sel_w[tid];
     }
   }
 

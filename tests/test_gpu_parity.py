@@ -224,17 +224,21 @@ def test_empty_input(toy_case):
     assert (out == 7.0).all()
 
 
-def test_group_large_and_invalid_ids():
-    rng = np.random.default_rng(21)
-    T, k, E = 2048, 8, 128
+@pytest.mark.parametrize("T,k,E", [(2048, 8, 128), (1000, 8, 128), (513, 8, 100), (129, 8, 128),
+                                   (1, 8, 128), (77, 2, 16)])
+def test_group_large_and_invalid_ids(T, k, E):
+    """Grouping against a stable argsort, with out-of-range ids (skipped).  1025 to
+    8192 entries over at most 128 experts take the single-pass kernel, the rest
+    the chunked one."""
+    rng = np.random.default_rng(21 + T)
     p = np.exp(-1.1 * np.log(np.arange(1, E + 1)))
     p /= p.sum()
     ids = np.stack([np.sort(rng.choice(E, size=k, replace=False, p=p)) for _ in range(T)])
     ids = ids.astype(np.int32)
     for bad in (False, True):
         if bad:
-            ids[3, 2] = E + 5
-            ids[100, 0] = -1
+            ids[min(3, T - 1), 1] = E + 5
+            ids[min(100, T - 1), 0] = -1
         offs = torch.empty(E + 1, dtype=torch.int32, device=DEV)
         rows = torch.empty(T * k, dtype=torch.int32, device=DEV)
         M.moe_group(dev(ids), E, offs, rows)
