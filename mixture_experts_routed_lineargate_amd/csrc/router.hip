@@ -107,39 +107,38 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restri
   const int tg = tid / 32, eg = tid % 32;     // tokens 4*tg.., experts 4*eg..
   float acc[4][4] = {};
   float sq[4] = {};                           // sum of x^2 over the slice, tokens 4*tg..
-  // A chunk's loads are all issued before any is used (clamped addresses, values
-  // masked afterwards), and the next chunk's are in flight during this chunk's FMAs.
-  float xr[XL], gr[GL];
-  auto load = [&](int dd) {
+  // Two chunks are in flight ahead of the FMAs (two register stages; clamped
+  // addresses, so every load is unconditional and values past the slice are
+  // masked at the LDS store): a 64-row slice costs one memory round trip.
+  struct Stage {
+    float x[XL], g[GL];
+  };
+  auto load = [&](int dd, Stage& st) {
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
       const int i = j * 256 + tid, tt = i / RT_K, c = i % RT_K;
       const int64_t t = min(t0 + tt, T - 1);
-      xr[j] = x[t * D + min(dd + c, D - 1)];
+      st.x[j] = x[t * D + min(dd + c, D - 1)];
     }
 #pragma unroll
     for (int j = 0; j < GL; ++j) {
       const int i = j * 256 + tid, c = i / RT_E, e = i % RT_E;
-      gr[j] = G[(int64_t)min(dd + c, D - 1) * E + min(e, E - 1)];
+      st.g[j] = G[(int64_t)min(dd + c, D - 1) * E + min(e, E - 1)];
     }
   };
-  auto store = [&](int dd) {
+  auto store = [&](int dd, const Stage& st) {
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
       const int i = j * 256 + tid, tt = i / RT_K, c = i % RT_K;
-      xs[c][tt] = (t0 + tt < T && dd + c < d1) ? xr[j] : 0.f;
+      xs[c][tt] = (t0 + tt < T && dd + c < d1) ? st.x[j] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < GL; ++j) {
       const int i = j * 256 + tid, c = i / RT_E, e = i % RT_E;
-      gs[c][e] = (e < E && dd + c < d1) ? gr[j] : 0.f;
+      gs[c][e] = (e < E && dd + c < d1) ? st.g[j] : 0.f;
     }
   };
-  load(d0);
-  for (int dd = d0; dd < d1; dd += RT_K) {
-    store(dd);
-    __syncthreads();
-    if (dd + RT_K < d1) load(dd + RT_K);
+  auto fma_chunk = [&]() {
 #pragma unroll 8
     for (int c = 0; c < RT_K; ++c) {
       const float4 xv = *(const float4*)&xs[c][4 * tg];
@@ -152,6 +151,21 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restri
         for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], ga[j], acc[i][j]);
       }
     }
+  };
+  Stage s0, s1;
+  load(d0, s0);
+  load(d0 + RT_K, s1);
+  for (int dd = d0; dd < d1; dd += 2 * RT_K) {
+    store(dd, s0);
+    __syncthreads();
+    load(dd + 2 * RT_K, s0);
+    fma_chunk();
+    __syncthreads();
+    if (dd + RT_K >= d1) break;                   // uniform
+    store(dd + RT_K, s1);
+    __syncthreads();
+    load(dd + 3 * RT_K, s1);
+    fma_chunk();
     __syncthreads();
   }
   if (ssq && eg == 0) {
@@ -187,6 +201,50 @@ hipError_t launch_router_partial(const float* x, int64_t T, int D, const float* 
   return hipGetLastError();
 }
 
+// Pick k winners by (value desc, index asc) with wave arg-max rounds, then
+// w_j = exp(l_j - l_max) / sum_selected exp(l - l_max), written in ascending id
+// order.  v[i] is the logit of expert i * WAVE + lane (-FLT_MAX past E).
+template <int PL>
+__device__ inline void select_and_write(const float (&v)[PL], int E, int k, int64_t t, int wave,
+                                        int lane, float (*sel_l)[MAX_K], int (*sel_e)[MAX_K],
+                                        int32_t* __restrict__ ids, float* __restrict__ w) {
+  uint32_t taken = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -FLT_MAX;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = i * WAVE + lane;
+      const bool ok = e < E && !((taken >> i) & 1u);
+      if (ok && (v[i] > bv || (v[i] == bv && e < be))) {
+        bv = v[i];
+        be = e;
+      }
+    }
+    // wave argmax: largest value, then the lowest index among equals
+    const float m = wave_max(bv);
+    be = wave_min(bv == m ? be : 0x7fffffff);
+    bv = m;
+    if ((be & (WAVE - 1)) == lane) taken |= 1u << (be / WAVE);
+    if (lane == 0) {
+      sel_l[wave][r] = bv;
+      sel_e[wave][r] = be;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  if (lane < k) {
+    const float lmax = sel_l[wave][0];
+    float den = 0.f;
+    for (int r = 0; r < k; ++r) den += expf(sel_l[wave][r] - lmax);
+    const int me = sel_e[wave][lane];
+    int rank = 0;
+    for (int r = 0; r < k; ++r) rank += sel_e[wave][r] < me;
+    ids[t * k + rank] = me;
+    w[t * k + rank] = expf(sel_l[wave][lane] - lmax) / den;
+  }
+}
+
 // One wavefront per token: sum the D-slice partials (fixed order), scale by the
 // RMSNorm factor when the router saw the raw input, add the bias, pick k
 // winners by (value desc, index asc), then weights
@@ -203,6 +261,77 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;  // whole wavefront leaves together; no block barrier below
+  // Common shapes (at most 32 D-slices, E <= 128, D <= 2048): every load of the
+  // token -- the per-slice sums of squares, the partial logits and the input
+  // row -- is issued before the first wait, so the token costs one memory round
+  // trip instead of three.  Indices are clamped, so the loads are unconditional.
+  if constexpr (PL <= 2) {
+  if (ksplit <= 32 && (!ex.xhi || ex.D <= 8 * 4 * WAVE)) {
+    float sv[32], pv[PL][32];
+    float4 q[8];
+    const float* xr = ex.x + t * ex.D;
+    if (ex.ssq) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) sv[j] = ex.ssq[(int64_t)min(j, ksplit - 1) * T + t];
+    }
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = min(i * WAVE + lane, E - 1);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) pv[i][j] = part[((int64_t)min(j, ksplit - 1) * T + t) * E + e];
+    }
+    if (ex.xhi) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = *(const float4*)(xr + min(4 * (j * WAVE + lane), ex.D - 4));
+    }
+    float inv = 1.0f;
+    if (ex.ssq) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (j < ksplit) ss += sv[j];
+      inv = 1.0f / sqrtf(ss / (float)ex.D + PRENORM_EPS);
+      if (ex.inv && lane == 0) ex.inv[t] = inv;
+    }
+    if (ex.xhi) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = 4 * (j * WAVE + lane);
+        if (d >= ex.D) break;
+        const float u[4] = {q[j].x * inv, q[j].y * inv, q[j].z * inv, q[j].w * inv};
+        _Float16 hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hi[i] = (_Float16)u[i];
+          lo[i] = (_Float16)(u[i] - (float)hi[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ex.xhi[t * ex.D + d + i] = hi[i];
+        if (ex.xlo) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ex.xlo[t * ex.D + d + i] = lo[i];
+        }
+      }
+    }
+    float v[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = i * WAVE + lane;
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (j < ksplit) sum += pv[i][j];                // slice order, as below
+      float l = -FLT_MAX;
+      if (e < E) {
+        l = sum * inv;
+        if (bias) l += bias[e];
+      }
+      v[i] = l;
+    }
+    select_and_write<PL>(v, E, k, t, wave, lane, sel_l, sel_e, ids, w);
+    return;
+  }
+  }
   // RMSNorm factor from the router's per-slice sums of squares (slice order)
   float inv = 1.0f;
   if (ex.ssq) {
@@ -270,41 +399,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
     }
     v[i] = s;
   }
-  uint32_t taken = 0;
-  for (int r = 0; r < k; ++r) {
-    float bv = -FLT_MAX;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int e = i * WAVE + lane;
-      const bool ok = e < E && !((taken >> i) & 1u);
-      if (ok && (v[i] > bv || (v[i] == bv && e < be))) {
-        bv = v[i];
-        be = e;
-      }
-    }
-    // wave argmax: largest value, then the lowest index among equals
-    const float m = wave_max(bv);
-    be = wave_min(bv == m ? be : 0x7fffffff);
-    bv = m;
-    if ((be & (WAVE - 1)) == lane) taken |= 1u << (be / WAVE);
-    if (lane == 0) {
-      sel_l[wave][r] = bv;
-      sel_e[wave][r] = be;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-  if (lane < k) {
-    const float lmax = sel_l[wave][0];
-    float den = 0.f;
-    for (int r = 0; r < k; ++r) den += expf(sel_l[wave][r] - lmax);
-    const int me = sel_e[wave][lane];
-    int rank = 0;
-    for (int r = 0; r < k; ++r) rank += sel_e[wave][r] < me;
-    ids[t * k + rank] = me;
-    w[t * k + rank] = expf(sel_l[wave][lane] - lmax) / den;
-  }
+  select_and_write<PL>(v, E, k, t, wave, lane, sel_l, sel_e, ids, w);
 }
 
 hipError_t launch_topk(const float* part, int ksplit, int64_t T, int E, const float* bias, int k,
