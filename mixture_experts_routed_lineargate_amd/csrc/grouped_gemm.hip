@@ -23,16 +23,18 @@
 //
 // Operands.  Activations arrive as fp16 planes (a = hi + lo, or hi alone when
 // single rounding is asked for), converted once per call rather than per tile.
-// Weights enter the MFMA as an exact pair of fp16 values per weight: the block
-// code q (or q - 8) is rebuilt as fp16 with the 0x6400 exponent trick, then
-// hi = fp16(d*q) and lo = fma(q, d, -hi), which is exact because d*q has at most
-// 19 significant bits.  So every MFMA accumulates straight into the fp32
-// accumulator (no per-block scaling pass): per 32-value block
-// acc += a_hi*(w_hi + w_lo) (+ a_lo*w_hi), and the only roundings are those of
-// the activations and fp32 accumulation.
+// Weights enter the MFMA as their exact integer codes (q, or q - 8 for 4-bit),
+// rebuilt as fp16 with the 0x6400 exponent trick.  One MFMA spans one 32-value
+// block, so per block t = a_hi . q (+ a_lo . q) comes out of one (two) MFMAs
+// with C = 0, and acc += d * t applies the block's fp16 scale: lane (.., ln) of
+// a 16x16 accumulator holds output column ln only, so it needs one scale per
+// block and n-subtile.  The products are exact; the roundings are those of the
+// activations, of fp32 accumulation and of the one FMA per block.  (An exact
+// hi/lo fp16 pair for d*q would need three MFMAs per block in split mode and
+// twice the dequantisation work; the scaled form is 7-10% faster end to end.)
 //
-// K loop: chunks of 2 blocks (64 values), prefetched into registers two chunks
-// ahead with unconditional loads, then written to one LDS buffer: activation
+// K loop: chunks of 2 blocks (64 values), the next one loaded into registers
+// while this one is multiplied, then written to one LDS buffer: activation
 // 16-byte pieces XOR-swizzled by row (conflict-free fragment reads), weight rows
 // transposed into dword slabs (thread t loads row t; padded slab stride keeps the
 // four lane groups of a fragment in distinct banks).
@@ -42,7 +44,6 @@ namespace moe {
 namespace gg {
 
 constexpr int NT = 256;               // threads per workgroup (4 wavefronts, two workgroups per CU)
-constexpr int NW = NT / WAVE;
 constexpr int BN = 256;               // weight rows per tile (64 per wavefront)
 constexpr int BKB = 2;                // blocks per K chunk
 constexpr int BK = BKB * QK;          // 64 values per K chunk
@@ -109,12 +110,6 @@ static int device_cus() {
   return cache[dev];
 }
 
-// Block b's weights as an exact fp16 pair, from a row in the slab layout.
-template <int FMT>
-__device__ inline void block_frag_hl(const uint32_t* col, int b, int g, h8& hi, h8& lo) {
-  frag_hl<FMT>([=](int off) { return wdw<FMT>(col, off); }, b, g, hi, lo);
-}
-
 // Persistent: each workgroup walks tiles L = slot, slot + G, ... where slot()
 // gives the workgroups of one XCD consecutive tiles (tiles are numbered M-tile
 // major, so an XCD works on a few M-tiles x their N-tiles at a time and can
@@ -124,7 +119,7 @@ __device__ inline void block_frag_hl(const uint32_t* col, int b, int g, h8& hi, 
 // into LDS in one batch, so the dependent index loads cost one round trip per
 // window rather than per tile.
 //
-// K pipeline: see the loop below (two register stages, one LDS buffer, two
+// K pipeline: see the loop below (one register stage, one LDS buffer, two
 // barriers per 64-value chunk; a second LDS buffer would cost the second
 // workgroup per CU).
 //
@@ -290,15 +285,22 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      // Per block: acc += a_hi (w_hi + w_lo) [+ a_lo w_hi].  The dropped a_lo * w_lo
-      // term is below 2^-22 of the product.
+      // Per block: t = (a_hi [+ a_lo]) . q on the exact integer codes, then
+      // acc += d * t with the block's fp16 scale d of the lane's column.
       auto compute = [&](const uint8_t* buf) {
         const uint32_t* bw = (const uint32_t*)(buf + PL * A_BYTES);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < BKB; ++b) {
-          h8 bh[4], bl[4];
+          h8 bq[4];
+          float dsc[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) block_frag_hl<FMT>(bw + wrow[s] + ln, b, lg, bh[s], bl[s]);
+          for (int s = 0; s < 4; ++s) {
+            const uint32_t* col = bw + wrow[s] + ln;
+            auto rd = [=](int off) { return wdw<FMT>(col, off); };
+            bq[s] = frag_codes<FMT>(rd, b, lg);
+            dsc[s] = frag_scale<FMT>(rd, b);
+          }
           h8 ah[MSUB], al[MSUB];
 #pragma unroll
           for (int m = 0; m < MSUB; ++m) {
@@ -310,43 +312,26 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
 #pragma unroll
           for (int m = 0; m < MSUB; ++m)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-              acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bh[s], acc[m][s], 0, 0, 0);
+            for (int s = 0; s < 4; ++s) {
+              f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bq[s], zero, 0, 0, 0);
+              if constexpr (SPLIT) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[m], bq[s], t, 0, 0, 0);
 #pragma unroll
-          for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bl[s], acc[m][s], 0, 0, 0);
-          if constexpr (SPLIT) {
-#pragma unroll
-            for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-              for (int s = 0; s < 4; ++s)
-                acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[m], bh[s], acc[m][s], 0, 0, 0);
-          }
+              for (int i = 0; i < 4; ++i) acc[m][s][i] = __builtin_fmaf(dsc[s], t[i], acc[m][s][i]);
+            }
         }
       };
 
-      // Two register stages are in flight at the loop head (chunk indices are clamped
-      // instead of skipping loads, so the compiler's wait counts stay exact); the LDS
-      // buffer is written, multiplied, and released once per chunk.
-      // (sched_barrier keeps each stage's loads together, so waiting for one stage
-      // never waits for the other)
-      Stage s0, s1;
+      // The next chunk's loads are issued before this chunk's MFMAs (indices
+      // clamped at the end, so every load is unconditional and the compiler's
+      // wait counts stay exact); the LDS buffer is written, multiplied and
+      // released once per chunk.  (A second register stage held more chunks in
+      // flight but pushed the kernel past 256 VGPRs.)
+      Stage s0;
       load(0, s0);
-      __builtin_amdgcn_sched_barrier(0);
-      load(1, s1);                                    // nchunks is even
-      __builtin_amdgcn_sched_barrier(0);
-      for (int c = 0; c < nchunks; c += 2) {
+      for (int c = 0; c < nchunks; ++c) {
         store(s0);
         __syncthreads();
-        load(min(c + 2, nchunks - 1), s0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(lds);
-        __syncthreads();
-        store(s1);
-        __syncthreads();
-        load(min(c + 3, nchunks - 1), s1);
+        load(min(c + 1, nchunks - 1), s0);
         __builtin_amdgcn_sched_barrier(0);
         compute(lds);
         __syncthreads();

@@ -1,8 +1,9 @@
 // Weight fragments for v_mfma_f32_16x16x32_f16 built from block-quantized rows
 // (shared by the grouped GEMM kernels).  A lane of a B fragment holds the 8
-// weights k = 8g .. 8g+7 of one weight row within a 32-value block; the row is
-// read through `rd(off)`, which returns the dword at byte offset `off` (a
-// multiple of 4) of the stored row, wherever the row sits in LDS.
+// weights k = 8g .. 8g+7 of one weight row within a 32-value block, as their
+// exact integer codes; the block's fp16 scale is applied to the MFMA result.
+// The row is read through `rd(off)`, which returns the dword at byte offset
+// `off` (a multiple of 4) of the stored row, wherever the row sits in LDS.
 #pragma once
 
 #include "internal.hpp"
@@ -65,20 +66,14 @@ __device__ inline h8 frag_codes(Rd rd, int b, int g) {
   return r.v;
 }
 
-// Block b's 8 weights k = 8g .. 8g+7 as an exact pair of fp16 vectors: d*q = hi + lo
-// with hi = fp16(d*q) and lo = d*q - hi (d*q has at most 19 significant bits, so lo
-// is exact; needs |d*q| < 65504, i.e. |d| < 511 for Q8_0 and |d| < 8187 for 4-bit).
+// Block b's fp16 scale d, as fp32.
 template <int FMT, typename Rd>
-__device__ inline void frag_hl(Rd rd, int b, int g, h8& hi, h8& lo) {
+__device__ inline float frag_scale(Rd rd, int b) {
   constexpr int BB = FMT == MOE_FMT_Q8_0 ? 34 : 18;
-  const h8 q = frag_codes<FMT>(rd, b, g);
   const int ob = b * BB;
   const uint32_t w = rd(ob & ~3);
   const uint16_t bits = (ob & 2) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
-  const _Float16 d = __builtin_bit_cast(_Float16, bits);
-  const h8 dd = {d, d, d, d, d, d, d, d};
-  hi = q * dd;
-  lo = __builtin_elementwise_fma(q, dd, -hi);
+  return (float)__builtin_bit_cast(_Float16, bits);
 }
 
 }  // namespace gg

@@ -1,7 +1,8 @@
 // Expert FFN on MFMA for few routed rows per expert (a decode batch: 32 tokens
 // x top-8 over 128 experts gives ~7 rows per active expert).  Same two stages
 // and the same operands as the grouped GEMM (grouped_gemm.hip): activations as
-// fp16 planes, weights as exact fp16 pairs (mfma_frag.hpp), fp32 accumulation.
+// fp16 planes, weights as exact integer codes with the block scale applied per
+// block after the MFMA (mfma_frag.hpp), fp32 accumulation.
 //
 // With so few rows the grouped GEMM's tiles (256 weight rows, a K loop of
 // 64-value chunks two deep) are few and latency-bound.  Here the weight slice
@@ -101,11 +102,14 @@ __device__ inline void pass_tiles(const Args& p, const uint8_t* wl, const int* m
 #pragma unroll
   for (int j = 0; j < G::BPW; ++j) {
     const int b = kb0 + j, slot = j % PDM;
-    h8 bh[G::NS], bl[G::NS];
+    h8 bq[G::NS];
+    float dsc[G::NS];
 #pragma unroll
     for (int s = 0; s < G::NS; ++s) {
       const uint32_t* rw = (const uint32_t*)(wl + (16 * s + ln) * G::RBP);
-      gg::frag_hl<FMT>([=](int off) { return rw[off >> 2]; }, b, lg, bh[s], bl[s]);
+      auto rd = [=](int off) { return rw[off >> 2]; };
+      bq[s] = gg::frag_codes<FMT>(rd, b, lg);
+      dsc[s] = gg::frag_scale<FMT>(rd, b);
     }
     h8 ah[MT], al[MT];
 #pragma unroll
@@ -114,15 +118,17 @@ __device__ inline void pass_tiles(const Args& p, const uint8_t* wl, const int* m
       if constexpr (SPLIT) al[m] = ra[slot][m][1];
     }
     if (j + PDM < G::BPW) aload(j + PDM, slot);
-    // acc += a_hi (w_hi + w_lo) [+ a_lo w_hi]; the dropped a_lo w_lo is below 2^-22
+    // t = (a_hi [+ a_lo]) . q on the exact codes, then acc += d * t (the block's
+    // scale of the lane's output column)
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int s = 0; s < G::NS; ++s) {
-        acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bh[s], acc[m][s], 0, 0, 0);
-        acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bl[s], acc[m][s], 0, 0, 0);
-        if constexpr (SPLIT)
-          acc[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[m], bh[s], acc[m][s], 0, 0, 0);
+        f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bq[s], zero, 0, 0, 0);
+        if constexpr (SPLIT) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[m], bq[s], t, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][s][i] = __builtin_fmaf(dsc[s], t[i], acc[m][s][i]);
       }
   }
 }
