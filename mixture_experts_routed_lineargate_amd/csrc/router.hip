@@ -11,7 +11,7 @@ namespace moe {
 // spreads the 1 MiB gate over many CUs.  Each slice is a multiple of 32 rows.
 int router_ksplit(int64_t T, int D) {
   const int64_t tiles = T >= 32 ? (T + 31) / 32 : (T + 7) / 8;
-  int64_t ks = 256 / (tiles > 0 ? tiles : 1);
+  int64_t ks = 512 / (tiles > 0 ? tiles : 1);     // ~two workgroups per CU
   if (ks > 32) ks = 32;            // the top-k pass sums ks partials per logit
   if (ks < 1) ks = 1;
   if (ks > D / 32) ks = D / 32;

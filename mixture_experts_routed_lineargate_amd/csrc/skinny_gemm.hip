@@ -133,8 +133,11 @@ __device__ inline void pass_tiles(const Args& p, const uint8_t* wl, const int* m
   }
 }
 
+// (at least two waves per SIMD, i.e. two workgroups per CU: with fewer the
+// compiler spends more registers and one workgroup's slice load is not
+// covered by the other's MFMAs)
 template <int FMT, int STAGE, bool SPLIT>
-__global__ __launch_bounds__(NT) void skinny_kernel(Args p) {
+__global__ __launch_bounds__(NT, 2) void skinny_kernel(Args p) {
   using G = Geo<FMT, STAGE>;
   __shared__ __attribute__((aligned(16))) uint8_t wl[G::W_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t red[G::RED_BYTES];
