@@ -231,7 +231,9 @@ def bench_prefill_down(torch, M, S, dev, stream, iters):
                        "(8192 rows x 768 fp32), 4-bit W_down 768x2048, Zipf routers; "
                        "rotating over 16 layers",
            "mean_active_experts": round(U, 2)}
-    for name, fl in (("split_fp16", 0), ("fp16", M.F_FP16_ACT)):
+    # split_fp16_banded: the same operator with the output tiles walked in bands of
+    # four (the reuse-ordering page's traversal; bit-identical results)
+    for name, fl in (("split_fp16", 0), ("fp16", M.F_FP16_ACT), ("split_fp16_banded", M.F_BANDED)):
         def one(fl=fl):
             for l in range(L4):
                 M.moe_expert_ffn(h, M.STAGE_DOWN, ex[l], ids[l], w[l], offs[l], rows[l],
@@ -393,7 +395,8 @@ def main():
     if "prefill_down" in want:
         extra["prefill_down"] = bench_prefill_down(torch, M, S, dev, stream, iters)
         print(f"[bench] prefill_down: {extra['prefill_down']['split_fp16']['ms_per_call'] * 1e3:.2f} "
-              f"/ {extra['prefill_down']['fp16']['ms_per_call'] * 1e3:.2f} us per call",
+              f"/ {extra['prefill_down']['fp16']['ms_per_call'] * 1e3:.2f} "
+              f"/ banded {extra['prefill_down']['split_fp16_banded']['ms_per_call'] * 1e3:.2f} us per call",
               file=sys.stderr, flush=True)
     if "prefill_stack" in want:
         extra["prefill_stack"] = bench_prefill_stack(torch, M, S, dev, stream, arena, gates,

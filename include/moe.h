@@ -80,9 +80,13 @@ enum {
   MOE_F_RESIDUAL = 1,      /* out += layer input                                       */
   MOE_F_DETERMINISTIC = 2, /* fp outputs bit-reproducible run to run                   */
   MOE_F_PRENORM = 4,       /* moe_layer only: the layer input is rmsnorm(x, eps=1e-6)   */
-  MOE_F_FP16_ACT = 8       /* MFMA expert kernels: round activations to fp16 once       */
+  MOE_F_FP16_ACT = 8,      /* MFMA expert kernels: round activations to fp16 once       */
                            /* instead of carrying them as two fp16 terms (hi + lo); half */
                            /* the matrix work, ~1e-3 RMS-relative output error           */
+  MOE_F_BANDED = 16        /* MFMA down projection: walk the output tiles in bands of   */
+                           /* four (reuse-ordering page, "What changed from the first    */
+                           /* experiment"); same per-tile arithmetic, so bit-identical   */
+                           /* results; off by default (no measured gain on MI355X)       */
 };
 
 /* One layer's experts (host struct holding device pointers).  Expert e's gate

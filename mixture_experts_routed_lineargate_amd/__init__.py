@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 MOE_OK = 0
 FMT_Q8_0, FMT_Q4 = 0, 1
 STAGE_FULL, STAGE_DOWN = 0, 1
-F_RESIDUAL, F_DETERMINISTIC, F_PRENORM, F_FP16_ACT = 1, 2, 4, 8
+F_RESIDUAL, F_DETERMINISTIC, F_PRENORM, F_FP16_ACT, F_BANDED = 1, 2, 4, 8, 16
 BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4: 18}
 
 

@@ -142,7 +142,8 @@ static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const 
     if (skinny)
       HIP_TRY(launch_skinny_down(hhi, hlo, a_mode, W, offsets, rows, R, k, ybuf, split, s));
     else
-      HIP_TRY(launch_grouped_down(hhi, hlo, a_mode, W, offsets, rows, R, k, ybuf, split, s));
+      HIP_TRY(launch_grouped_down(hhi, hlo, a_mode, W, offsets, rows, R, k, ybuf, split, s,
+                                  (flags & MOE_F_BANDED) != 0));
     if (out) HIP_TRY(launch_combine(ybuf, w, T, k, W.D, res, out, s, res_scale));
     return MOE_OK;
   }
@@ -200,7 +201,7 @@ static moe_status layer_impl(const float* x, const float* gate, const float* bia
     HIP_TRY(launch_topk(w.part_logits, ks, T, E, bias, k, ids, wts, s, ex));
     HIP_TRY(launch_group(ids, T * k, E, offs, rows, s));
     return do_ffn(x, MOE_STAGE_FULL, dev, ids, wts, offs, rows, T, k, nullptr, out,
-                  flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC | MOE_F_FP16_ACT), w, s,
+                  flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC | MOE_F_FP16_ACT | MOE_F_BANDED), w, s,
                   /*planes_ready=*/true, pre ? w.inv : nullptr);
   }
   trace("layer generic", T, D, F, E, k, W->format);
@@ -212,7 +213,7 @@ static moe_status layer_impl(const float* x, const float* gate, const float* bia
   MOE_TRY(do_route(u, T, D, gate, bias, E, k, ids, wts, w, s));
   HIP_TRY(launch_group(ids, T * k, E, offs, rows, s));
   return do_ffn(u, MOE_STAGE_FULL, dev, ids, wts, offs, rows, T, k, nullptr, out,
-                flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC | MOE_F_FP16_ACT), w, s);
+                flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC | MOE_F_FP16_ACT | MOE_F_BANDED), w, s);
 }
 
 }  // namespace moe

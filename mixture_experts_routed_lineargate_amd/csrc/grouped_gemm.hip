@@ -65,6 +65,7 @@ struct Args {
   int E, N, K;               // N = output columns (d_ff for gate/up, d_model for down)
   int R;                     // rows (T * k); offsets and rows are clamped to it
   int n_tiles;
+  int band;                  // 0: M-tile major; B: N-tiles in bands of B (B divides n_tiles)
   _Float16* ohi;             // gate/up: h planes [R][N] in sorted order
   _Float16* olo;
   float* y;                  // down: y [R][N] in flat order
@@ -179,8 +180,17 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
   const int nchunks = p.K / BK;                     // even (K is a multiple of 128)
 
   auto decode_tile = [&](int L, int& e, int& row0, int& nrows, int& nt) {
-    const int mg = L / p.n_tiles;
-    nt = L % p.n_tiles;
+    int mg;
+    if (p.band > 0) {
+      // band bi holds N-tiles bi*band .. +band-1 of every M-tile, M-tile major inside
+      const int per_band = total_m * p.band;
+      const int bi = L / per_band, r = L % per_band;
+      mg = r / p.band;
+      nt = bi * p.band + r % p.band;
+    } else {
+      mg = L / p.n_tiles;
+      nt = L % p.n_tiles;
+    }
     int lo_e = 0, hi_e = E - 1;                     // last e with tstart[e] <= mg
     while (lo_e < hi_e) {
       const int mid = (lo_e + hi_e + 1) >> 1;
@@ -433,7 +443,8 @@ hipError_t launch_grouped_gateup(const _Float16* xhi, const _Float16* xlo, int a
 
 hipError_t launch_grouped_down(const _Float16* hhi, const _Float16* hlo, int a_mode,
                                const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
-                               int64_t R, int k, float* y, bool split, hipStream_t s) {
+                               int64_t R, int k, float* y, bool split, hipStream_t s,
+                               bool banded) {
   if (R <= 0) return hipSuccess;
   gg::Args p{};
   p.ahi = hhi;
@@ -449,6 +460,7 @@ hipError_t launch_grouped_down(const _Float16* hhi, const _Float16* hlo, int a_m
   p.N = W.D;
   p.K = W.F;
   p.n_tiles = W.D / gg::BN;
+  p.band = (banded && p.n_tiles % 4 == 0) ? 4 : 0;
   p.y = y;
   const bool sm = grouped_small_m(R);
   return W.fmt == MOE_FMT_Q8_0 ? gg::launch_f<MOE_FMT_Q8_0, gg::STAGE_DOWN>(p, R, sm, split, s)

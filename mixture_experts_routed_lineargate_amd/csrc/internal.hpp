@@ -157,7 +157,8 @@ hipError_t launch_grouped_gateup(const _Float16* xhi, const _Float16* xlo, int a
                                  hipStream_t s);
 hipError_t launch_grouped_down(const _Float16* hhi, const _Float16* hlo, int a_mode,
                                const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
-                               int64_t R, int k, float* y, bool split, hipStream_t s);
+                               int64_t R, int k, float* y, bool split, hipStream_t s,
+                               bool banded = false);
 hipError_t launch_to_planes(const float* src, int64_t n, _Float16* hi, _Float16* lo,
                             hipStream_t s);
 // few rows per expert (R <= 512) at the tuned geometry: weight-slice kernels, same operands

@@ -141,6 +141,30 @@ def test_prefill_down_parity(down_case, flags):
     check_out(out.cpu().numpy(), c.ref)
 
 
+def test_prefill_down_banded_is_bit_identical(down_case):
+    """The banded tile walk (reuse-ordering page) changes only the order in which
+    workgroups take tiles, so y and out match the default walk bit for bit, and
+    the oracle like every other mode."""
+    c = down_case
+    T, k = c.T, c.k
+    ids, w = dev(c.ids), dev(c.w)
+    offs = torch.empty(c.E + 1, dtype=torch.int32, device=DEV)
+    rows = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    ws = M.workspace(T, c.D, c.F, c.E, k, c.fmt)
+    M.moe_group(ids, c.E, offs, rows, ws)
+    res = []
+    for flags in (0, M.F_BANDED):
+        y = torch.full((T * k, c.D), float("nan"), dtype=torch.float32, device=DEV)
+        out = torch.empty((T, c.D), dtype=torch.float32, device=DEV)
+        M.moe_expert_ffn(dev(c.h), M.STAGE_DOWN, experts_of(c), ids, w, offs, rows, y=y, out=out,
+                         flags=flags, ws=ws)
+        torch.cuda.synchronize()
+        res.append((y.cpu().numpy(), out.cpu().numpy()))
+    assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
+    assert np.array_equal(res[0][1].view(np.uint32), res[1][1].view(np.uint32))
+    check_out(res[1][1], c.ref)
+
+
 def test_prefill_layer_sampled_tokens():
     """1024-token Q8_0 layer at Qwen geometry; the oracle checks a sample of tokens
     (tokens are independent through one layer)."""
