@@ -397,15 +397,20 @@ __device__ inline void select_top8_block(const float* lg, int* top, int* sel_e, 
   const int tid = threadIdx.x;
   const int e = tid >> 2, q = tid & 3;
   const float le = lg[e];
-  int cnt = 0;
+  // VALU-only counts: logits above le, and logits equal to le (itself included);
+  // the index tie-break runs only where le has an exact duplicate
+  int cnt = 0, eq = 0;
 #pragma unroll
   for (int i = 0; i < 32; i += 4) {
     const float4 v = *(const float4*)(lg + 32 * q + i);
-    const int e2 = 32 * q + i;
-    cnt += (v.x > le) | ((v.x == le) & (e2 + 0 < e));
-    cnt += (v.y > le) | ((v.y == le) & (e2 + 1 < e));
-    cnt += (v.z > le) | ((v.z == le) & (e2 + 2 < e));
-    cnt += (v.w > le) | ((v.w == le) & (e2 + 3 < e));
+    cnt += (v.x > le) + (v.y > le) + (v.z > le) + (v.w > le);
+    eq += (v.x == le) + (v.y == le) + (v.z == le) + (v.w == le);
+  }
+  eq += dpp<DPP_QUAD_1032>(eq);
+  eq += dpp<DPP_QUAD_2301>(eq);
+  if (eq > 1) {
+#pragma unroll 1
+    for (int i = 0; i < 32; ++i) cnt += (lg[32 * q + i] == le) & (32 * q + i < e);
   }
   cnt += dpp<DPP_QUAD_1032>(cnt);
   cnt += dpp<DPP_QUAD_2301>(cnt);
