@@ -189,17 +189,24 @@ static moe_status layer_impl(const float* x, const float* gate, const float* bia
     trace("layer grouped (fused norm + planes)", T, D, F, E, k, W->format);
     const bool pre = (flags & MOE_F_PRENORM) != 0;
     const bool split = !(flags & MOE_F_FP16_ACT);
-    const int ks = router_ksplit(T, D);
-    HIP_TRY(launch_router_partial(x, T, D, gate, E, w.part_logits, ks, s, pre ? w.ssq : nullptr));
-    TopkExtra ex;
-    ex.ssq = pre ? w.ssq : nullptr;
-    ex.D = D;
-    ex.inv = pre ? w.inv : nullptr;
-    ex.x = x;
-    ex.xhi = w.xp;
-    ex.xlo = split ? w.xp + (size_t)T * D : nullptr;
-    HIP_TRY(launch_topk(w.part_logits, ks, T, E, bias, k, ids, wts, s, ex));
-    HIP_TRY(launch_group(ids, T * k, E, offs, rows, s));
+    _Float16* xlo = split ? w.xp + (size_t)T * D : nullptr;
+    if (route_small_supported(T, D, E, k)) {
+      // small batch: router, top-k and grouping in one launch
+      HIP_TRY(launch_route_small(x, T, D, gate, bias, E, k, pre, ids, wts, pre ? w.inv : nullptr,
+                                 w.xp, xlo, offs, rows, w, s));
+    } else {
+      const int ks = router_ksplit(T, D);
+      HIP_TRY(launch_router_partial(x, T, D, gate, E, w.part_logits, ks, s, pre ? w.ssq : nullptr));
+      TopkExtra ex;
+      ex.ssq = pre ? w.ssq : nullptr;
+      ex.D = D;
+      ex.inv = pre ? w.inv : nullptr;
+      ex.x = x;
+      ex.xhi = w.xp;
+      ex.xlo = xlo;
+      HIP_TRY(launch_topk(w.part_logits, ks, T, E, bias, k, ids, wts, s, ex));
+      HIP_TRY(launch_group(ids, T * k, E, offs, rows, s));
+    }
     return do_ffn(x, MOE_STAGE_FULL, dev, ids, wts, offs, rows, T, k, nullptr, out,
                   flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC | MOE_F_FP16_ACT | MOE_F_BANDED), w, s,
                   /*planes_ready=*/true, pre ? w.inv : nullptr);

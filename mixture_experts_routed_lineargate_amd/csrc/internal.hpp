@@ -113,7 +113,8 @@ struct Workspace {
 
 int router_ksplit(int64_t T, int D);
 Workspace carve_workspace(void* base, int64_t T, int D, int F, int E, int k, int flags);
-constexpr size_t SYNC_BYTES = 2 * 1024 * 1024;  // barrier words and exchange buffers
+constexpr size_t SYNC_BYTES = 4 * 1024 * 1024;  // barrier words and exchange buffers
+constexpr size_t ROUTE_SYNC_OFF = 2 * 1024 * 1024;  // small-batch routing's exchange words
 
 bool trace_enabled();
 void trace(const char* what, int64_t T, int D, int F, int E, int k, int fmt);
@@ -135,6 +136,13 @@ struct TopkExtra {
 };
 hipError_t launch_topk(const float* part, int ksplit, int64_t T, int E, const float* bias, int k,
                        int32_t* ids, float* w, hipStream_t s, const TopkExtra& ex = TopkExtra());
+// Router + top-k (+ RMSNorm factor and input planes) + grouping of at most 32
+// tokens in one launch (route_small.hip).
+bool route_small_supported(int64_t T, int D, int E, int k);
+hipError_t launch_route_small(const float* x, int64_t T, int D, const float* G, const float* bias,
+                              int E, int k, bool prenorm, int32_t* ids, float* w, float* inv,
+                              _Float16* xhi, _Float16* xlo, int32_t* offsets, int32_t* rows,
+                              const Workspace& ws, hipStream_t s);
 hipError_t launch_group(const int32_t* ids, int64_t N, int E, int32_t* offsets, int32_t* rows,
                         hipStream_t s);
 hipError_t launch_gateup_generic(const float* x, const ExpertsDev& W, const int32_t* ids, int64_t T,

@@ -3,7 +3,7 @@
 // learned LinearGate selection; Model card: top-8 of 128 experts.)
 #include <float.h>
 
-#include "internal.hpp"
+#include "topk_select.hpp"
 
 namespace moe {
 
@@ -199,50 +199,6 @@ hipError_t launch_router_partial(const float* x, int64_t T, int D, const float* 
   hipLaunchKernelGGL(router_partial_kernel<8>, grid, dim3(256), 0, s, x, T, D, G, E, dchunk, part,
                      ssq);
   return hipGetLastError();
-}
-
-// Pick k winners by (value desc, index asc) with wave arg-max rounds, then
-// w_j = exp(l_j - l_max) / sum_selected exp(l - l_max), written in ascending id
-// order.  v[i] is the logit of expert i * WAVE + lane (-FLT_MAX past E).
-template <int PL>
-__device__ inline void select_and_write(const float (&v)[PL], int E, int k, int64_t t, int wave,
-                                        int lane, float (*sel_l)[MAX_K], int (*sel_e)[MAX_K],
-                                        int32_t* __restrict__ ids, float* __restrict__ w) {
-  uint32_t taken = 0;
-  for (int r = 0; r < k; ++r) {
-    float bv = -FLT_MAX;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int e = i * WAVE + lane;
-      const bool ok = e < E && !((taken >> i) & 1u);
-      if (ok && (v[i] > bv || (v[i] == bv && e < be))) {
-        bv = v[i];
-        be = e;
-      }
-    }
-    // wave argmax: largest value, then the lowest index among equals
-    const float m = wave_max(bv);
-    be = wave_min(bv == m ? be : 0x7fffffff);
-    bv = m;
-    if ((be & (WAVE - 1)) == lane) taken |= 1u << (be / WAVE);
-    if (lane == 0) {
-      sel_l[wave][r] = bv;
-      sel_e[wave][r] = be;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-  if (lane < k) {
-    const float lmax = sel_l[wave][0];
-    float den = 0.f;
-    for (int r = 0; r < k; ++r) den += expf(sel_l[wave][r] - lmax);
-    const int me = sel_e[wave][lane];
-    int rank = 0;
-    for (int r = 0; r < k; ++r) rank += sel_e[wave][r] < me;
-    ids[t * k + rank] = me;
-    w[t * k + rank] = expf(sel_l[wave][lane] - lmax) / den;
-  }
 }
 
 // One wavefront per token: sum the D-slice partials (fixed order), scale by the
