@@ -21,8 +21,9 @@
  *  - Ownership: the caller owns every buffer, including the workspace `ws`
  *    (size from moe_workspace_bytes).  The library allocates no device memory
  *    and keeps no mutable state between calls other than inside `ws`: the
- *    first 64 KiB of a workspace hold grid-barrier counters of the fused
- *    kernels, so a workspace must be zero-filled once before its first use
+ *    first 4 MiB of a workspace hold the launch counters and tagged exchange
+ *    words of the fused kernels (single-token decode, decode stack, small-batch
+ *    routing), so a workspace must be zero-filled once before its first use
  *    and must not be shared by calls that may run concurrently (calls that
  *    share a workspace must be stream-ordered).
  *  - Errors: arguments are validated on the host before anything is enqueued;
