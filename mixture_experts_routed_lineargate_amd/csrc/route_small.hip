@@ -31,15 +31,17 @@ using dec::SPIN_LIMIT;
 using dec::gather_fn;
 using dec::publish;
 
-constexpr int NT = 256;
+constexpr int NT = 512;
 constexpr int SL = 64;              // rows of d_model per slice
 constexpr int NS_MAX = 32;          // slices (d_model <= 2048)
 constexpr int TMAX = 32;            // tokens
 constexpr int EMAX = 128;           // experts (two logits per lane of one wavefront)
 constexpr int EP = 136;             // words per (slice, token): E partials, sum of squares at E
 constexpr int KMAX = 8;
+constexpr int TQ = TMAX * EMAX / NT;   // tokens per thread in R
 constexpr int QW = (NS_MAX * (EMAX + 1) + NT - 1) / NT;   // gathered words per thread in S
-static_assert(TMAX * SL % NT == 0 && TMAX <= NT && EMAX + 1 <= EP && TMAX * KMAX <= NT, "shape");
+static_assert(TMAX * SL % NT == 0 && SL * EMAX % NT == 0 && 2048 / 4 % NT == 0 && TMAX <= NT &&
+                  EMAX + 1 <= EP && TMAX * KMAX <= NT && TQ * (NT / EMAX) == TMAX, "shape");
 
 struct Args {
   const float* x;                   // [T][D]
@@ -61,7 +63,7 @@ struct Args {
 };
 
 __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
-  __shared__ float xs[TMAX][SL + 1];
+  __shared__ __attribute__((aligned(16))) float xs[TMAX][SL + 4];   // rows 16-byte aligned
   __shared__ float gs[SL][EMAX];
   __shared__ float pl[NS_MAX * (EMAX + 1)];
   __shared__ float sums[EMAX + 1];
@@ -77,6 +79,10 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
   const int T = p.T, D = p.D, E = p.E, k = p.k;
   uint32_t budget = SPIN_LIMIT;
   const uint32_t tg = __hip_atomic_load(p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  // the bias is read now: read at the top-k it would cost a memory latency there
+  float bv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) bv[i] = p.bias ? p.bias[min(i * WAVE + lane, E - 1)] : 0.f;
 
   // ---- R: partial logits of slice s ----
   // (loads first, all unconditional: clamped rows and columns, masked at use)
@@ -114,19 +120,25 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
     gs[i / EMAX][i % EMAX] = gv[j];
   }
   __syncthreads();
-  const int e = tid % EMAX, th = tid / EMAX;     // expert, token half (tokens 16 th ..)
-  float acc[TMAX / 2];
+  const int e = tid % EMAX, th = tid / EMAX;     // expert, token group (tokens TQ th ..)
+  float acc[TQ];
 #pragma unroll
-  for (int i = 0; i < TMAX / 2; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < SL; ++c) {
-    const float g = gs[c][e];
+  for (int i = 0; i < TQ; ++i) acc[i] = 0.f;
+#pragma unroll 2
+  for (int c = 0; c < SL; c += 4) {
+    const float g[4] = {gs[c][e], gs[c + 1][e], gs[c + 2][e], gs[c + 3][e]};
 #pragma unroll
-    for (int i = 0; i < TMAX / 2; ++i) acc[i] = fmaf(xs[th * (TMAX / 2) + i][c], g, acc[i]);
+    for (int i = 0; i < TQ; ++i) {
+      const float4 xq = *(const float4*)&xs[th * TQ + i][c];
+      acc[i] = fmaf(xq.x, g[0], acc[i]);
+      acc[i] = fmaf(xq.y, g[1], acc[i]);
+      acc[i] = fmaf(xq.z, g[2], acc[i]);
+      acc[i] = fmaf(xq.w, g[3], acc[i]);
+    }
   }
 #pragma unroll
-  for (int i = 0; i < TMAX / 2; ++i) {
-    const int t = th * (TMAX / 2) + i;
+  for (int i = 0; i < TQ; ++i) {
+    const int t = th * TQ + i;
     if (t < T && e < E) publish(p.xp + ((int64_t)s * TMAX + t) * EP + e, tg, acc[i]);
   }
   if (tid < T) {
@@ -152,6 +164,7 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
     __syncthreads();
     if (tid <= E) {
       float a = 0.f;
+#pragma unroll 8
       for (int q = 0; q < ns; ++q) a += pl[q * (E + 1) + tid];   // slice order
       sums[tid] = a;
     }
@@ -165,7 +178,7 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
         float l = -FLT_MAX;
         if (ee < E) {
           l = sums[ee] * inv;
-          if (p.bias) l += p.bias[ee];
+          if (p.bias) l += bv[i];
         }
         v[i] = l;
       }
