@@ -111,7 +111,7 @@ static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const 
   const bool full = stage == MOE_STAGE_FULL;
   const int64_t R = T * k;
   auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
-  if (grouped_supported(W, full) && a16(in) && a16(y) && a16(out)) {
+  if (grouped_supported(W, full) && grouped_fits(T, R, W) && a16(in) && a16(y) && a16(out)) {
     const bool split = !(flags & MOE_F_FP16_ACT);
     const bool skinny = skinny_supported(W, R, full);
     trace(full ? (split ? "ffn grouped mfma gate/up+down (split fp16)"
@@ -182,7 +182,8 @@ static moe_status layer_impl(const float* x, const float* gate, const float* bia
     return MOE_OK;
   }
   auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
-  if (grouped_supported(dev, true) && a16(x) && a16(out) && D % 4 == 0) {
+  if (grouped_supported(dev, true) && grouped_fits(T, T * k, dev) && a16(x) && a16(out) &&
+      D % 4 == 0) {
     // MFMA path: the router also sums x^2 per slice; the top-k pass forms the
     // RMSNorm factor, the routing, and the fp16 planes of the normalised input, so
     // neither a normalisation pass nor a separate conversion pass runs

@@ -33,11 +33,16 @@
 // hi/lo fp16 pair for d*q would need three MFMAs per block in split mode and
 // twice the dequantisation work; the scaled form is 7-10% faster end to end.)
 //
-// K loop: chunks of 2 blocks (64 values), the next one loaded into registers
-// while this one is multiplied, then written to one LDS buffer: activation
-// 16-byte pieces XOR-swizzled by row (conflict-free fragment reads), weight rows
-// transposed into dword slabs (thread t loads row t; padded slab stride keeps the
-// four lane groups of a fragment in distinct banks).
+// K loop: chunks of 2 blocks (64 values).  Activation chunks go from global
+// memory straight into a ring of three LDS buffers (global_load_lds, 16-byte
+// pieces XOR-swizzled by row so fragment reads are conflict-free), two chunks
+// ahead, shared by the four wavefronts.  Weights never touch LDS: each lane loads
+// the dwords of its own fragment (the four lanes of a row read 12 + 8 bytes of
+// the row's two blocks) one chunk ahead, and the block scales come from the lanes
+// that hold them (ds_bpermute).  The weight loads are interleaved with the MFMAs
+// so that the texture-address unit, which spends about the same time on every
+// 64-lane load whatever its width, sees a steady stream instead of bursts.  A
+// tile whose rows fill fewer than four 16-row subtiles multiplies only those.
 #include "mfma_frag.hpp"
 
 namespace moe {
@@ -71,18 +76,80 @@ struct Args {
   float* y;                  // down: y [R][N] in flat order
 };
 
-// A chunk of weight rows sits in LDS transposed: slab u holds dword u of all
-// BN rows (thread t loads row t, one dword per slab), slabs SLAB dwords apart.
-// SLAB = 256 + 8 (Q8_0) / 256 + 16 (4-bit) puts the dwords that the four lane
-// groups of a fragment read (2 / 1 dwords apart) in distinct banks.
+// One K chunk (two blocks) of a stored weight row, read straight into the MFMA
+// B-fragment layout: lane group g takes codes 8g .. 8g+7 of each block, plus the
+// dwords that hold the two block scales.  A chunk starts 4-byte aligned (rows
+// are whole 16-byte units and a chunk is 68 / 36 bytes), so block 0's codes sit
+// 2 bytes past a dword boundary and are realigned with alignbyte; block 1's are
+// dword aligned.
+__device__ inline float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ inline float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
 template <int FMT>
-struct Fmt {
-  static constexpr int BB = FMT == MOE_FMT_Q8_0 ? 34 : 18;
-  static constexpr int CB = BKB * BB;          // bytes of one row in one K chunk (68 / 36)
-  static constexpr int U4 = CB / 4;            // dwords per row chunk = dword loads per thread
-  static constexpr int SLAB = BN + (FMT == MOE_FMT_Q8_0 ? 8 : 16);
-  static_assert(CB % 4 == 0 && BN == NT, "one weight row per thread, whole dwords");
+struct Fmt;
+
+template <>
+struct Fmt<MOE_FMT_Q8_0> {
+  static constexpr int BB = 34;                // [d (fp16)][32 int8 codes]
+  static constexpr int CB = BKB * BB;          // 68 bytes per row per chunk: dwords D0 .. D16
+  struct Raw {
+    uint32_t c0[3];                            // D2g .. D2g+2: block 0 codes 8g .. 8g+7 at byte 2
+    uint32_t c1[2];                            // D9+2g, D10+2g: block 1 codes 8g .. 8g+7
+  };
+  // base: the chunk of the subtile's first row (uniform); lrow: byte offset of the
+  // lane's row from it
+  __device__ static void load(const uint8_t* base, uint32_t lrow, int g, Raw& r) {
+    const uint32_t* wg = (const uint32_t*)(base + (lrow + 8u * g));
+#pragma unroll
+    for (int i = 0; i < 3; ++i) r.c0[i] = wg[i];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r.c1[i] = wg[9 + i];
+  }
+  // The scales sit in D0 (lane group 0's c0[0], low half) and D8 (lane group 3's
+  // c0[2], high half); ln is the lane's row within the subtile.
+  __device__ static void decode(const Raw& r, int ln, h8& q0, h8& q1, float& s0, float& s1) {
+    q0 = codes_q8(__builtin_amdgcn_alignbyte(r.c0[1], r.c0[0], 2),
+                  __builtin_amdgcn_alignbyte(r.c0[2], r.c0[1], 2));
+    q1 = codes_q8(r.c1[0], r.c1[1]);
+    s0 = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute(ln * 4, (int)r.c0[0]));
+    s1 = half_hi((uint32_t)__builtin_amdgcn_ds_bpermute((ln + 48) * 4, (int)r.c0[2]));
+  }
 };
+
+template <>
+struct Fmt<MOE_FMT_Q4> {
+  static constexpr int BB = 18;                // [d (fp16)][16 bytes of nibbles]
+  static constexpr int CB = BKB * BB;          // 36 bytes per row per chunk: dwords D0 .. D8
+  struct Raw {
+    uint32_t c0[2];                            // Dg, Dg+1: block 0 nibble bytes 4g .. 4g+3 at byte 2
+    uint32_t c1;                               // D5+g: block 1 nibble bytes 4g .. 4g+3
+  };
+  __device__ static void load(const uint8_t* base, uint32_t lrow, int g, Raw& r) {
+    const uint32_t* wg = (const uint32_t*)(base + (lrow + 4u * g));
+    r.c0[0] = wg[0];
+    r.c0[1] = wg[1];
+    r.c1 = wg[5];
+  }
+  // The scales sit in D0 (lane group 0's c0[0], low half) and D4 (lane group 3's
+  // c0[1], high half).
+  __device__ static void decode(const Raw& r, int ln, h8& q0, h8& q1, float& s0, float& s1) {
+    q0 = codes_q4(__builtin_amdgcn_alignbyte(r.c0[1], r.c0[0], 2));
+    q1 = codes_q4(r.c1);
+    s0 = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute(ln * 4, (int)r.c0[0]));
+    s1 = half_hi((uint32_t)__builtin_amdgcn_ds_bpermute((ln + 48) * 4, (int)r.c0[1]));
+  }
+};
+
+// global_load_lds_dwordx4: lane i of the wavefront writes the 16 bytes at
+// base + off (base wavefront-uniform, off a per-lane byte offset below 2^31) to
+// LDS bytes lds + 16i .. 16i+15 (lds wavefront-uniform).  Issued from asm so the
+// compiler neither orders LDS reads behind it nor counts it: callers wait with an
+// explicit vmcnt, or through a later load that completes after it.
+__device__ inline void lds_dma16(const void* base, uint32_t off, const uint8_t* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(a)
+               : "memory");
+}
 
 __device__ inline int xcd_swizzle(int bid, int total) {
   // bid = 8 s + x runs on XCD x; give XCD x a contiguous range of tiles
@@ -90,11 +157,6 @@ __device__ inline int xcd_swizzle(int bid, int total) {
   const int q = total >> 3, r = total & 7;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + s;
 }
-
-// Dword at byte offset off (a multiple of 4) of a weight row stored as a column
-// of the slab layout.
-template <int FMT>
-__device__ inline uint32_t wdw(const uint32_t* col, int off) { return col[(off >> 2) * Fmt<FMT>::SLAB]; }
 
 // Compute units of the current device (cached per device).
 static int device_cus() {
@@ -120,9 +182,9 @@ static int device_cus() {
 // into LDS in one batch, so the dependent index loads cost one round trip per
 // window rather than per tile.
 //
-// K pipeline: see the loop below (one register stage, one LDS buffer, two
-// barriers per 64-value chunk; a second LDS buffer would cost the second
-// workgroup per CU).
+// K pipeline: see the loop below (activations two chunks ahead in a ring of
+// three LDS buffers, weights one chunk ahead in registers, one barrier per
+// 64-value chunk).
 //
 // Wavefront w computes 64 rows x 64 weight rows (4 x 4 MFMA tiles): down rows
 // 64w .. 64w+63, or gate rows 32w .. 32w+31 (subtiles 0, 1) and the up rows
@@ -137,16 +199,18 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
   constexpr int PL = SPLIT ? 2 : 1;                 // activation planes
   constexpr int A_BYTES = BM * BK * 2;              // one plane of one chunk
   constexpr int A_DMA = BM * (BK / 8) >= NT ? BM * (BK / 8) / NT : 1;   // 16-byte loads / plane
-  constexpr int B_BYTES = FF::U4 * FF::SLAB * 4;
-  constexpr int BUF = PL * A_BYTES + B_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[BUF];
+  constexpr int A_SLOTS = BM * (BK / 8);            // 16-byte pieces of one plane of one chunk
+  constexpr int BUF = PL * A_BYTES;
+  constexpr int NBUF = 3;                           // activation chunks in LDS
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * BUF];
   __shared__ int offs[MAX_E + 1];                   // expert_offsets clamped to [0, R]
   __shared__ int tstart[MAX_E + 1];                 // M-tiles of experts < e
   __shared__ int total_m;
   __shared__ int m_src[TW][BM];                     // activation row (always a valid row)
   __shared__ int m_flat[TW][BM];                    // flat row t*k+j, -1 = padding
 
-  const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+  const int tid = threadIdx.x, lane = tid % WAVE;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int E = p.E;
   for (int e = tid; e <= E; e += NT) offs[e] = min(max(p.offsets[e], 0), p.R);
   __syncthreads();
@@ -211,6 +275,7 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
       wrow[s] = wave * 64 + s * 16;
   }
   const int ln = lane % 16, lg = lane / 16;
+  const uint32_t lrow = (uint32_t)(ln * RB);        // this lane's weight row within a subtile
 
   for (int k0 = 0; k0 < ntiles; k0 += TW) {
     // ---- metadata of the window's tiles ----
@@ -240,6 +305,11 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
       if (k0 + w >= ntiles) break;                    // uniform over the workgroup
       int e, row0, nrows, nt;
       decode_tile(first + (k0 + w) * G, e, row0, nrows, nt);
+      e = __builtin_amdgcn_readfirstlane(e);          // the tile is the workgroup's: make its
+      row0 = __builtin_amdgcn_readfirstlane(row0);    // fields scalar so every address below
+      nrows = __builtin_amdgcn_readfirstlane(nrows);  // is a scalar base + lane offset
+      nt = __builtin_amdgcn_readfirstlane(nt);
+      const int msub = (nrows + 15) / 16;             // 16-row subtiles holding rows
       int n0;
       const uint8_t* hb0;
       const uint8_t* hb1;
@@ -252,124 +322,147 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
         hb0 = p.w0 + (int64_t)e * p.s0 + (int64_t)n0 * RB;
         hb1 = hb0 + (int64_t)(BN / 2) * RB;
       }
+      // first weight row of n-subtile s (wavefront-uniform)
+      const uint8_t* sb[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sb[s] = wrow[s] < BN / 2 ? hb0 + (int64_t)wrow[s] * RB : hb1 + (int64_t)(wrow[s] - BN / 2) * RB;
+
       // activation 16-byte pieces of this thread: slot q = i*NT + tid (mod the slots of a
       // plane) is row q / 8, stored piece q % 8, holding logical piece (q % 8) ^ swz(row)
-      int64_t aoff[A_DMA];
+      uint32_t aoff[A_DMA];                           // byte offsets (planes are below 2 GiB)
 #pragma unroll
       for (int i = 0; i < A_DMA; ++i) {
         const int q = (i * NT + tid) % (BM * (BK / 8));
         const int r = q / 8, c = (q % 8) ^ ((r >> 1) & 7);
-        aoff[i] = (int64_t)m_src[w][r] * p.K + 8 * c;
+        aoff[i] = ((uint32_t)m_src[w][r] * (uint32_t)p.K + 8u * c) * 2u;
       }
-
-      const uint8_t* brow = tid < BN / 2 ? hb0 + (int64_t)tid * RB : hb1 + (int64_t)(tid - BN / 2) * RB;
-      struct Stage {
-        u32x4 a[PL][A_DMA];
-        uint32_t b[FF::U4];
-      };
-      auto load = [&](int c, Stage& st) {
+      // Activation chunk c goes straight from global memory into LDS buffer `buf`
+      // (global_load_lds: lane i of a wavefront fills bytes 16i .. 16i+15 of the
+      // wavefront's 1 KiB destination, so slot q = i*NT + tid lands at 16q).
+      auto load_a = [&](int c, uint8_t* buf) {
+        if (A_SLOTS >= NT || wave * WAVE < A_SLOTS) {   // wavefront-uniform
 #pragma unroll
-        for (int pl = 0; pl < PL; ++pl) {
-          const _Float16* src = (pl ? p.alo : p.ahi) + c * BK;
+          for (int pl = 0; pl < PL; ++pl) {
+            const _Float16* src = (pl ? p.alo : p.ahi) + c * BK;
 #pragma unroll
-          for (int i = 0; i < A_DMA; ++i) st.a[pl][i] = *(const u32x4*)(src + aoff[i]);
-        }
-        const uint32_t* bsrc = (const uint32_t*)(brow + c * FF::CB);
-#pragma unroll
-        for (int u = 0; u < FF::U4; ++u) st.b[u] = bsrc[u];
-      };
-      auto store = [&](const Stage& st) {
-#pragma unroll
-        for (int pl = 0; pl < PL; ++pl)
-#pragma unroll
-          for (int i = 0; i < A_DMA; ++i)
-            *(u32x4*)(lds + pl * A_BYTES + ((i * NT + tid) % (BM * (BK / 8))) * 16) = st.a[pl][i];
-        uint32_t* bw = (uint32_t*)(lds + PL * A_BYTES) + tid;     // weight row tid
-#pragma unroll
-        for (int u = 0; u < FF::U4; ++u) bw[u * FF::SLAB] = st.b[u];
-      };
-
-      f32x4 acc[MSUB][4];
-#pragma unroll
-      for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-      // Per block: t = (a_hi [+ a_lo]) . q on the exact integer codes, then
-      // acc += d * t with the block's fp16 scale d of the lane's column.
-      auto compute = [&](const uint8_t* buf) {
-        const uint32_t* bw = (const uint32_t*)(buf + PL * A_BYTES);
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < BKB; ++b) {
-          h8 bq[4];
-          float dsc[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const uint32_t* col = bw + wrow[s] + ln;
-            auto rd = [=](int off) { return wdw<FMT>(col, off); };
-            bq[s] = frag_codes<FMT>(rd, b, lg);
-            dsc[s] = frag_scale<FMT>(rd, b);
+            for (int i = 0; i < A_DMA; ++i)
+              lds_dma16(src, aoff[i], buf + pl * A_BYTES + (i * NT + wave * WAVE) * 16);
           }
-          h8 ah[MSUB], al[MSUB];
+        }
+      };
+
+      // Weight dwords of one K chunk (two blocks) for the lane's row of each n-subtile,
+      // loaded straight into the fragment layout (lane group lg takes k = 8lg .. 8lg+7 of
+      // each block), plus the two dwords holding the block scales.
+      typename FF::Raw braw[4];
+      auto load_b = [&](int c) {
 #pragma unroll
-          for (int m = 0; m < MSUB; ++m) {
+        for (int s = 0; s < 4; ++s) FF::load(sb[s] + (int64_t)c * FF::CB, lrow, lg, braw[s]);
+      };
+
+      // The K loop and epilogue of one tile whose rows fill MS 16-row subtiles.
+      auto run_tile = [&](auto MSc) {
+        constexpr int MS = decltype(MSc)::value;
+        f32x4 acc[MS][4];
+#pragma unroll
+        for (int m = 0; m < MS; ++m)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // Per block: t = (a_hi [+ a_lo]) . q on the exact integer codes, then
+        // acc += d * t with the block's fp16 scale d of the lane's column.
+        auto compute = [&](const uint8_t* buf, const h8 (&bq)[BKB][4], const float (&dsc)[BKB][4]) {
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < MS; ++m) {
+            h8 ah[BKB], al[BKB];
             const int r = m * 16 + ln;
-            const int o = r * (BK * 2) + ((((QK / 8) * b + lg) ^ ((r >> 1) & 7)) * 16);
-            ah[m] = *(const h8*)(buf + o);
-            if constexpr (SPLIT) al[m] = *(const h8*)(buf + A_BYTES + o);
-          }
 #pragma unroll
-          for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bq[s], zero, 0, 0, 0);
-              if constexpr (SPLIT) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[m], bq[s], t, 0, 0, 0);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[m][s][i] = __builtin_fmaf(dsc[s], t[i], acc[m][s][i]);
+            for (int b = 0; b < BKB; ++b) {
+              const int o = r * (BK * 2) + ((((QK / 8) * b + lg) ^ ((r >> 1) & 7)) * 16);
+              ah[b] = *(const h8*)(buf + o);
+              if constexpr (SPLIT) al[b] = *(const h8*)(buf + A_BYTES + o);
             }
+#pragma unroll
+            for (int b = 0; b < BKB; ++b)
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[b], bq[b][s], zero, 0, 0, 0);
+                if constexpr (SPLIT) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[b], bq[b][s], t, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[m][s][i] = __builtin_fmaf(dsc[b][s], t[i], acc[m][s][i]);
+              }
+          }
+        };
+
+        // One chunk: decode this chunk's weights (the wait for them also covers the
+        // activation chunk requested before them: loads complete in issue order),
+        // request the activations two chunks ahead (into the LDS buffer freed by the
+        // previous chunk) and the weights one chunk ahead, multiply, one barrier
+        // (which publishes the next activation chunk to every wavefront).  Indices
+        // are clamped at the end, so every load is unconditional.
+        load_a(0, lds);
+        load_a(min(1, nchunks - 1), lds + BUF);
+        load_b(0);
+        __builtin_amdgcn_s_waitcnt(0x0f70);          // vmcnt(0)
+        __syncthreads();
+        int bc = 0;                                   // buffer of chunk c
+        for (int c = 0; c < nchunks; ++c) {
+          const uint8_t* cur = lds + bc * BUF;
+          const int b2 = bc == 0 ? 2 : bc - 1;        // buffer of chunk c + 2
+          h8 bq[BKB][4];
+          float dsc[BKB][4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) FF::decode(braw[s], ln, bq[0][s], bq[1][s], dsc[0][s], dsc[1][s]);
+          __builtin_amdgcn_sched_barrier(0);
+          load_a(min(c + 2, nchunks - 1), lds + b2 * BUF);
+          load_b(min(c + 1, nchunks - 1));
+          compute(cur, bq, dsc);
+          // spread the weight loads over the multiplies
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MS * (SPLIT ? 2 : 1), 0);
+          }
+          __syncthreads();
+          bc = bc == 2 ? 0 : bc + 1;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);          // the clamped tail loads
+
+        // ---- epilogue: lane holds rows 16m + 4*lg + i, column ln of each n-subtile ----
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = m * 16 + 4 * lg + i;
+            const int fl = m_flat[w][r];
+            if (fl < 0) continue;                       // padding row
+            if constexpr (STAGE == STAGE_GATEUP) {
+#pragma unroll
+              for (int s = 0; s < 2; ++s) {
+                const int64_t o = (int64_t)(row0 + r) * p.N + n0 + wave * 32 + s * 16 + ln;
+                const float hv = silu(acc[m][s][i]) * acc[m][s + 2][i];
+                const _Float16 hh = (_Float16)hv;
+                p.ohi[o] = hh;
+                if constexpr (SPLIT) p.olo[o] = (_Float16)(hv - (float)hh);
+              }
+            } else {
+              float* yrow = p.y + (int64_t)fl * p.N + n0 + ln;
+#pragma unroll
+              for (int s = 0; s < 4; ++s) yrow[wrow[s]] = acc[m][s][i];
+            }
+          }
         }
       };
-
-      // The next chunk's loads are issued before this chunk's MFMAs (indices
-      // clamped at the end, so every load is unconditional and the compiler's
-      // wait counts stay exact); the LDS buffer is written, multiplied and
-      // released once per chunk.  (A second register stage held more chunks in
-      // flight but pushed the kernel past 256 VGPRs.)
-      Stage s0;
-      load(0, s0);
-      for (int c = 0; c < nchunks; ++c) {
-        store(s0);
-        __syncthreads();
-        load(min(c + 1, nchunks - 1), s0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(lds);
-        __syncthreads();
-      }
-
-      // ---- epilogue: lane holds rows 16m + 4*lg + i, column ln of each n-subtile ----
-#pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = m * 16 + 4 * lg + i;
-          const int fl = m_flat[w][r];
-          if (fl < 0) continue;                         // padding row
-          if constexpr (STAGE == STAGE_GATEUP) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const int64_t o = (int64_t)(row0 + r) * p.N + n0 + wave * 32 + s * 16 + ln;
-              const float hv = silu(acc[m][s][i]) * acc[m][s + 2][i];
-              const _Float16 hh = (_Float16)hv;
-              p.ohi[o] = hh;
-              if constexpr (SPLIT) p.olo[o] = (_Float16)(hv - (float)hh);
-            }
-          } else {
-            float* yrow = p.y + (int64_t)fl * p.N + n0 + ln;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) yrow[wrow[s]] = acc[m][s][i];
-          }
-        }
+      if constexpr (MSUB == 1) {
+        run_tile(std::integral_constant<int, 1>{});
+      } else {
+        static_assert(MSUB == 4, "tiles of 16 or 64 rows");
+        if (msub == 4) run_tile(std::integral_constant<int, 4>{});
+        else if (msub == 3) run_tile(std::integral_constant<int, 3>{});
+        else if (msub == 2) run_tile(std::integral_constant<int, 2>{});
+        else run_tile(std::integral_constant<int, 1>{});
       }
       __syncthreads();                                  // metadata / buffers reused next
     }
@@ -411,6 +504,12 @@ bool grouped_supported(const ExpertsDev& W, bool need_gate_up) {
 }
 
 bool grouped_small_m(int64_t R) { return R <= 2048; }
+
+// The activation planes are addressed with 32-bit byte offsets.
+bool grouped_fits(int64_t T, int64_t R, const ExpertsDev& W) {
+  const int64_t lim = (int64_t)1 << 31;
+  return T * (int64_t)W.D * 2 < lim && R * (int64_t)W.F * 2 < lim && R * (int64_t)W.D * 2 < lim;
+}
 
 hipError_t launch_grouped_gateup(const _Float16* xhi, const _Float16* xlo, int a_mode,
                                  const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,

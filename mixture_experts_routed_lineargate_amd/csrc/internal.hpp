@@ -159,6 +159,7 @@ hipError_t launch_rmsnorm(const float* x, int64_t T, int D, float eps, float* ou
 enum { GG_A_TOKEN = 0, GG_A_FLAT = 1, GG_A_SORTED = 2 };   // activation row of sorted row i:
                                                           // x[rows[i]/k], h[rows[i]], h[i]
 bool grouped_supported(const ExpertsDev& W, bool need_gate_up);
+bool grouped_fits(int64_t T, int64_t R, const ExpertsDev& W);
 hipError_t launch_grouped_gateup(const _Float16* xhi, const _Float16* xlo, int a_mode,
                                  const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
                                  int64_t R, int k, _Float16* hhi, _Float16* hlo, bool split,

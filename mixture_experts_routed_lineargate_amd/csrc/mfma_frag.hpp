@@ -15,15 +15,49 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
-// Block b's weights k = 8g .. 8g+7 as exact fp16 codes (q, or q - 8).
-template <int FMT, typename Rd>
-__device__ inline h8 frag_codes(Rd rd, int b, int g) {
-  constexpr int BB = FMT == MOE_FMT_Q8_0 ? 34 : 18;
+// Eight signed Q8_0 codes (bytes of q0, then q1) as exact fp16 values.
+__device__ inline h8 codes_q8(uint32_t q0, uint32_t q1) {
   union {
     uint32_t u[4];
     h2 p[4];
     h8 v;
   } r;
+  // two's complement -> biased unsigned, then 0x64uu = 1024 + u as fp16
+  q0 ^= 0x80808080u;
+  q1 ^= 0x80808080u;
+  r.u[0] = __builtin_amdgcn_perm(0x64646464u, q0, 0x04010400u);
+  r.u[1] = __builtin_amdgcn_perm(0x64646464u, q0, 0x04030402u);
+  r.u[2] = __builtin_amdgcn_perm(0x64646464u, q1, 0x04010400u);
+  r.u[3] = __builtin_amdgcn_perm(0x64646464u, q1, 0x04030402u);
+  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};   // 1024 + 128
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.p[i] = r.p[i] - bias;
+  return r.v;
+}
+
+// Eight 4-bit codes (byte j holds element 2j in its low nibble, 2j+1 in its
+// high nibble) as the exact fp16 values q - 8.
+__device__ inline h8 codes_q4(uint32_t n) {
+  union {
+    uint32_t u[4];
+    h2 p[4];
+    h8 v;
+  } r;
+  const uint32_t lo = n & 0x0f0f0f0fu, hi = (n >> 4) & 0x0f0f0f0fu;
+  r.u[0] = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x64006400u;
+  r.u[1] = __builtin_amdgcn_perm(hi, lo, 0x0c050c01u) | 0x64006400u;
+  r.u[2] = __builtin_amdgcn_perm(hi, lo, 0x0c060c02u) | 0x64006400u;
+  r.u[3] = __builtin_amdgcn_perm(hi, lo, 0x0c070c03u) | 0x64006400u;
+  const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};   // 1024 + 8
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.p[i] = r.p[i] - bias;
+  return r.v;
+}
+
+// Block b's weights k = 8g .. 8g+7 as exact fp16 codes (q, or q - 8).
+template <int FMT, typename Rd>
+__device__ inline h8 frag_codes(Rd rd, int b, int g) {
+  constexpr int BB = FMT == MOE_FMT_Q8_0 ? 34 : 18;
   if constexpr (FMT == MOE_FMT_Q8_0) {
     const int s = b * BB + 2 + 8 * g;                  // 2 mod 4 when b is even
     uint32_t q0, q1;
@@ -35,16 +69,7 @@ __device__ inline h8 frag_codes(Rd rd, int b, int g) {
       q0 = rd(s);
       q1 = rd(s + 4);
     }
-    // two's complement -> biased unsigned, then 0x64uu = 1024 + u as fp16
-    q0 ^= 0x80808080u;
-    q1 ^= 0x80808080u;
-    r.u[0] = __builtin_amdgcn_perm(0x64646464u, q0, 0x04010400u);
-    r.u[1] = __builtin_amdgcn_perm(0x64646464u, q0, 0x04030402u);
-    r.u[2] = __builtin_amdgcn_perm(0x64646464u, q1, 0x04010400u);
-    r.u[3] = __builtin_amdgcn_perm(0x64646464u, q1, 0x04030402u);
-    const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};   // 1024 + 128
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.p[i] = r.p[i] - bias;
+    return codes_q8(q0, q1);
   } else {
     const int s = b * BB + 2 + 4 * g;                  // 2 mod 4 when b is even
     uint32_t n;
@@ -53,17 +78,8 @@ __device__ inline h8 frag_codes(Rd rd, int b, int g) {
     } else {
       n = rd(s);
     }
-    // byte j holds element 2j (low nibble) and 2j+1 (high nibble)
-    const uint32_t lo = n & 0x0f0f0f0fu, hi = (n >> 4) & 0x0f0f0f0fu;
-    r.u[0] = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x64006400u;
-    r.u[1] = __builtin_amdgcn_perm(hi, lo, 0x0c050c01u) | 0x64006400u;
-    r.u[2] = __builtin_amdgcn_perm(hi, lo, 0x0c060c02u) | 0x64006400u;
-    r.u[3] = __builtin_amdgcn_perm(hi, lo, 0x0c070c03u) | 0x64006400u;
-    const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};   // 1024 + 8
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.p[i] = r.p[i] - bias;
+    return codes_q4(n);
   }
-  return r.v;
 }
 
 // Block b's fp16 scale d, as fp32.
