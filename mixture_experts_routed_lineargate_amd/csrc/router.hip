@@ -85,11 +85,16 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const float* __rest
   }
 }
 
-// Register-tiled fp32 router GEMM for many tokens and E <= 128 experts:
-// part[s][t][e] over the s-th slice of d.  A workgroup owns 32 tokens x 128
-// experts of one slice; each thread accumulates 4 tokens x 4 experts, reading
-// x and G from LDS in 32-row chunks.  G is read from HBM once per token tile
-// (it stays in the L2 across the 32-token tiles of a slice).
+// fp32 MFMA router GEMM for many tokens and E <= 128 experts (E a multiple of 4,
+// D of 32, x and G 16-byte aligned): part[s][t][e]
+// over the s-th slice of d.  A workgroup owns 32 tokens x 128 experts of one
+// slice; x and G pass through LDS in 32-row chunks (two chunks in flight ahead
+// of the multiplies).  Wavefront w takes tokens 16*(w&1) .. +15 and experts
+// 64*(w>>1) .. +63 as four 16x16 tiles of v_mfma_f32_16x16x4_f32 (fp32 products
+// and sums).  Within each 16-row step of a chunk, MFMA j has lane group g
+// supply row 4g + j, so every operand read is one conflict-free dword; the four
+// MFMAs of a step cover the step's 16 rows.  G stays in the L2 across the
+// 32-token tiles of a slice.
 constexpr int RT_T = 32, RT_E = 128, RT_K = 32;
 
 __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restrict__ x, int64_t T,
@@ -97,58 +102,72 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restri
                                                            int E, int dchunk,
                                                            float* __restrict__ part,
                                                            float* __restrict__ ssq) {
-  __shared__ float xs[RT_K][RT_T + 4];        // [k][token], padded
+  __shared__ float xs[RT_K][RT_T + 4];        // [row][token], padded
   __shared__ __attribute__((aligned(16))) float gs[RT_K][RT_E];
   constexpr int XL = RT_T * RT_K / 256, GL = RT_K * RT_E / 256;   // loads per thread per chunk
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid % WAVE;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int th = wave & 1, eh = wave >> 1;    // token half, expert half
+  const int ln = lane % 16, lg = lane / 16;
   const int64_t t0 = (int64_t)blockIdx.x * RT_T;
   const int sl = blockIdx.y;
   const int d0 = sl * dchunk, d1 = min(D, d0 + dchunk);
-  const int tg = tid / 32, eg = tid % 32;     // tokens 4*tg.., experts 4*eg..
-  float acc[4][4] = {};
-  float sq[4] = {};                           // sum of x^2 over the slice, tokens 4*tg..
-  // Two chunks are in flight ahead of the FMAs (two register stages; clamped
-  // addresses, so every load is unconditional and values past the slice are
-  // masked at the LDS store): a 64-row slice costs one memory round trip.
+  f32x4 acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float sq = 0.f;                             // x^2 over this lane's rows, token 16*th + ln
+  // Two register stages of 16-byte loads (clamped addresses, so every load is
+  // unconditional; values past the slice or the token range are masked at the LDS
+  // store): a 64-row slice costs one memory round trip.
+  constexpr int XL4 = XL / 4, GL4 = GL / 4;
   struct Stage {
-    float x[XL], g[GL];
+    float4 x[XL4], g[GL4];
   };
   auto load = [&](int dd, Stage& st) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j) {
-      const int i = j * 256 + tid, tt = i / RT_K, c = i % RT_K;
+    for (int j = 0; j < XL4; ++j) {
+      const int i = j * 256 + tid, tt = i / (RT_K / 4), c = 4 * (i % (RT_K / 4));
       const int64_t t = min(t0 + tt, T - 1);
-      st.x[j] = x[t * D + min(dd + c, D - 1)];
+      st.x[j] = *(const float4*)(x + t * D + min(dd + c, D - 4));
     }
 #pragma unroll
-    for (int j = 0; j < GL; ++j) {
-      const int i = j * 256 + tid, c = i / RT_E, e = i % RT_E;
-      st.g[j] = G[(int64_t)min(dd + c, D - 1) * E + min(e, E - 1)];
+    for (int j = 0; j < GL4; ++j) {
+      const int i = j * 256 + tid, c = i / (RT_E / 4), e = 4 * (i % (RT_E / 4));
+      st.g[j] = *(const float4*)(G + (int64_t)min(dd + c, D - 1) * E + min(e, E - 4));
     }
   };
   auto store = [&](int dd, const Stage& st) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j) {
-      const int i = j * 256 + tid, tt = i / RT_K, c = i % RT_K;
-      xs[c][tt] = (t0 + tt < T && dd + c < d1) ? st.x[j] : 0.f;
+    for (int j = 0; j < XL4; ++j) {
+      const int i = j * 256 + tid, tt = i / (RT_K / 4), c = 4 * (i % (RT_K / 4));
+      const bool ok = t0 + tt < T && dd + c < d1;    // d1 - dd is a multiple of 4
+      xs[c][tt] = ok ? st.x[j].x : 0.f;
+      xs[c + 1][tt] = ok ? st.x[j].y : 0.f;
+      xs[c + 2][tt] = ok ? st.x[j].z : 0.f;
+      xs[c + 3][tt] = ok ? st.x[j].w : 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < GL; ++j) {
-      const int i = j * 256 + tid, c = i / RT_E, e = i % RT_E;
-      gs[c][e] = (e < E && dd + c < d1) ? st.g[j] : 0.f;
+    for (int j = 0; j < GL4; ++j) {
+      const int i = j * 256 + tid, c = i / (RT_E / 4), e = 4 * (i % (RT_E / 4));
+      const bool ok = e < E && dd + c < d1;          // E is a multiple of 4
+      *(float4*)&gs[c][e] = ok ? st.g[j] : float4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto fma_chunk = [&]() {
-#pragma unroll 8
-    for (int c = 0; c < RT_K; ++c) {
-      const float4 xv = *(const float4*)&xs[c][4 * tg];
-      const float4 gv = *(const float4*)&gs[c][4 * eg];
-      const float xa[4] = {xv.x, xv.y, xv.z, xv.w}, ga[4] = {gv.x, gv.y, gv.z, gv.w};
+  auto mfma_chunk = [&]() {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sq[i] = fmaf(xa[i], xa[i], sq[i]);
+    for (int kk = 0; kk < RT_K; kk += 16) {
+      float a[4], b[4][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], ga[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) {
+        a[j] = xs[kk + 4 * lg + j][16 * th + ln];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) b[n][j] = gs[kk + 4 * lg + j][64 * eh + 16 * n + ln];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sq = fmaf(a[j], a[j], sq);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[n][j], acc[n], 0, 0, 0);
       }
     }
   };
@@ -159,30 +178,31 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restri
     store(dd, s0);
     __syncthreads();
     load(dd + 2 * RT_K, s0);
-    fma_chunk();
+    mfma_chunk();
     __syncthreads();
     if (dd + RT_K >= d1) break;                   // uniform
     store(dd + RT_K, s1);
     __syncthreads();
     load(dd + 3 * RT_K, s1);
-    fma_chunk();
+    mfma_chunk();
     __syncthreads();
   }
-  if (ssq && eg == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = t0 + 4 * tg + i;
-      if (t < T) ssq[(int64_t)sl * T + t] = sq[i];
-    }
+  // the four lane groups hold disjoint rows of token 16*th + ln
+  sq += __shfl_xor(sq, 16, WAVE);
+  sq += __shfl_xor(sq, 32, WAVE);
+  if (ssq && eh == 0 && lg == 0) {
+    const int64_t t = t0 + 16 * th + ln;
+    if (t < T) ssq[(int64_t)sl * T + t] = sq;
   }
+  // lane (ln, lg) holds tokens 4*lg + i of the wave's half, expert ln of tile n
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t t = t0 + 4 * tg + i;
+    const int64_t t = t0 + 16 * th + 4 * lg + i;
     if (t >= T) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * eg + j;
-      if (e < E) part[((int64_t)sl * T + t) * E + e] = acc[i][j];
+    for (int n = 0; n < 4; ++n) {
+      const int e = 64 * eh + 16 * n + ln;
+      if (e < E) part[((int64_t)sl * T + t) * E + e] = acc[n][i];
     }
   }
 }
@@ -190,7 +210,8 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restri
 hipError_t launch_router_partial(const float* x, int64_t T, int D, const float* G, int E,
                                  float* part, int ksplit, hipStream_t s, float* ssq) {
   const int dchunk = router_dchunk(D, ksplit);
-  if (E <= RT_E && T >= RT_T) {
+  auto a16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+  if (E <= RT_E && T >= RT_T && E % 4 == 0 && D % 32 == 0 && a16(x) && a16(G)) {
     dim3 grid((unsigned)((T + RT_T - 1) / RT_T), (unsigned)ksplit);
     hipLaunchKernelGGL(router_tiled_kernel, grid, dim3(256), 0, s, x, T, D, G, E, dchunk, part, ssq);
     return hipGetLastError();
