@@ -76,81 +76,6 @@ struct Args {
   float* y;                  // down: y [R][N] in flat order
 };
 
-// One K chunk (two blocks) of a stored weight row, read straight into the MFMA
-// B-fragment layout: lane group g takes codes 8g .. 8g+7 of each block, plus the
-// dwords that hold the two block scales.  A chunk starts 4-byte aligned (rows
-// are whole 16-byte units and a chunk is 68 / 36 bytes), so block 0's codes sit
-// 2 bytes past a dword boundary and are realigned with alignbyte; block 1's are
-// dword aligned.
-__device__ inline float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
-__device__ inline float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
-
-template <int FMT>
-struct Fmt;
-
-template <>
-struct Fmt<MOE_FMT_Q8_0> {
-  static constexpr int BB = 34;                // [d (fp16)][32 int8 codes]
-  static constexpr int CB = BKB * BB;          // 68 bytes per row per chunk: dwords D0 .. D16
-  struct Raw {
-    uint32_t c0[3];                            // D2g .. D2g+2: block 0 codes 8g .. 8g+7 at byte 2
-    uint32_t c1[2];                            // D9+2g, D10+2g: block 1 codes 8g .. 8g+7
-  };
-  // base: the chunk of the subtile's first row (uniform); lrow: byte offset of the
-  // lane's row from it
-  __device__ static void load(const uint8_t* base, uint32_t lrow, int g, Raw& r) {
-    const uint32_t* wg = (const uint32_t*)(base + (lrow + 8u * g));
-#pragma unroll
-    for (int i = 0; i < 3; ++i) r.c0[i] = wg[i];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) r.c1[i] = wg[9 + i];
-  }
-  // The scales sit in D0 (lane group 0's c0[0], low half) and D8 (lane group 3's
-  // c0[2], high half); ln is the lane's row within the subtile.
-  __device__ static void decode(const Raw& r, int ln, h8& q0, h8& q1, float& s0, float& s1) {
-    q0 = codes_q8(__builtin_amdgcn_alignbyte(r.c0[1], r.c0[0], 2),
-                  __builtin_amdgcn_alignbyte(r.c0[2], r.c0[1], 2));
-    q1 = codes_q8(r.c1[0], r.c1[1]);
-    s0 = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute(ln * 4, (int)r.c0[0]));
-    s1 = half_hi((uint32_t)__builtin_amdgcn_ds_bpermute((ln + 48) * 4, (int)r.c0[2]));
-  }
-};
-
-template <>
-struct Fmt<MOE_FMT_Q4> {
-  static constexpr int BB = 18;                // [d (fp16)][16 bytes of nibbles]
-  static constexpr int CB = BKB * BB;          // 36 bytes per row per chunk: dwords D0 .. D8
-  struct Raw {
-    uint32_t c0[2];                            // Dg, Dg+1: block 0 nibble bytes 4g .. 4g+3 at byte 2
-    uint32_t c1;                               // D5+g: block 1 nibble bytes 4g .. 4g+3
-  };
-  __device__ static void load(const uint8_t* base, uint32_t lrow, int g, Raw& r) {
-    const uint32_t* wg = (const uint32_t*)(base + (lrow + 4u * g));
-    r.c0[0] = wg[0];
-    r.c0[1] = wg[1];
-    r.c1 = wg[5];
-  }
-  // The scales sit in D0 (lane group 0's c0[0], low half) and D4 (lane group 3's
-  // c0[1], high half).
-  __device__ static void decode(const Raw& r, int ln, h8& q0, h8& q1, float& s0, float& s1) {
-    q0 = codes_q4(__builtin_amdgcn_alignbyte(r.c0[1], r.c0[0], 2));
-    q1 = codes_q4(r.c1);
-    s0 = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute(ln * 4, (int)r.c0[0]));
-    s1 = half_hi((uint32_t)__builtin_amdgcn_ds_bpermute((ln + 48) * 4, (int)r.c0[1]));
-  }
-};
-
-// global_load_lds_dwordx4: lane i of the wavefront writes the 16 bytes at
-// base + off (base wavefront-uniform, off a per-lane byte offset below 2^31) to
-// LDS bytes lds + 16i .. 16i+15 (lds wavefront-uniform).  Issued from asm so the
-// compiler neither orders LDS reads behind it nor counts it: callers wait with an
-// explicit vmcnt, or through a later load that completes after it.
-__device__ inline void lds_dma16(const void* base, uint32_t off, const uint8_t* lds) {
-  const uint32_t a = (uint32_t)(uintptr_t)lds;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(a)
-               : "memory");
-}
-
 __device__ inline int xcd_swizzle(int bid, int total) {
   // bid = 8 s + x runs on XCD x; give XCD x a contiguous range of tiles
   const int x = bid & 7, s = bid >> 3;
