@@ -199,6 +199,29 @@ def test_prefill_down_banded_is_bit_identical(down_case):
     check_out(res[1][1], c.ref)
 
 
+@pytest.mark.parametrize("T,E,fmt", [
+    (100, 100, 0),   # MFMA router with 100 experts and a ragged 32-token tile; 16-row GEMM tiles
+    (70, 98, 1),     # 98 experts (not a multiple of 4): the FMA router for many tokens
+    (300, 100, 1),   # 64-row GEMM tiles (some partly filled) with 100 experts
+])
+def test_many_token_shapes(T, E, fmt):
+    """Routing of every token against the oracle's router; layer output on a sample
+    of tokens that includes the ragged last router tile."""
+    c = cases.router_case(f"many{T}", 200 + T, T, 2048, 768, E, 8, fmt, True, DEV)
+    g = run_layer(c, M.F_RESIDUAL)
+    logits = O.router_logits(c.x, c.G, c.b)
+    ids = O.select_topk(logits, c.k)
+    assert np.array_equal(g["ids"], ids), "expert ids differ"
+    assert np.abs(g["w"] - O.routing_weights(logits, ids)).max() <= W_TOL
+    roff, rrows = O.group(g["ids"], c.E)
+    assert np.array_equal(g["offsets"], roff) and np.array_equal(g["sorted_rows"], rrows)
+    rng = np.random.default_rng(T)
+    sample = np.unique(np.concatenate([rng.choice(T, size=10, replace=False),
+                                       np.arange(T - 3, T)]))
+    r = O.moe_layer(c.x[sample], c.G, c.b, c.oracle_experts(), c.k, residual=True)
+    check_out(g["out"][sample], r["out"])
+
+
 def test_prefill_layer_sampled_tokens():
     """1024-token Q8_0 layer at Qwen geometry; the oracle checks a sample of tokens
     (tokens are independent through one layer)."""
