@@ -159,13 +159,22 @@ def n_active(torch, ids) -> int:
     return int(torch.unique(ids).numel())
 
 
-def rates(ms: float, nbytes: float, flops: float) -> dict:
+def rates(ms: float, nbytes: float, flops: float, ffn: float = 0.0, split: bool = True) -> dict:
+    """Algorithmic rates; `ffn` = the expert-FFN share of `flops`.  With split fp16
+    activations every algorithmic product costs two fp16 MFMA products, so the
+    dequant-adjusted peak for the expert FFN is half the fp16 peak (fp16-only
+    activations: the full peak)."""
     s = ms / 1e3
     gbps = nbytes / s / 1e9
     tf = flops / s / 1e12
-    return {"ms_per_call": round(ms, 5), "algorithmic_bytes": int(nbytes),
-            "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-            "mfma_tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_FP16_PEAK_TFLOPS, 4)}
+    r = {"ms_per_call": round(ms, 5), "algorithmic_bytes": int(nbytes),
+         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+         "mfma_tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_FP16_PEAK_TFLOPS, 4)}
+    if ffn > 0:
+        adj = MFMA_FP16_PEAK_TFLOPS / (2.0 if split else 1.0)
+        r["ffn_mfma_adjusted_peak_tflops"] = round(adj, 1)
+        r["ffn_mfma_adjusted_frac"] = round(ffn / s / 1e12 / adj, 4)
+    return r
 
 
 def ffn_flops(rows: int) -> float:
@@ -197,7 +206,7 @@ def bench_decode_batch(torch, M, S, dev, stream, iters):
     r = {"workload": "decode batch: 32 tokens x Qwen3-MoE layer, 4-bit experts, Zipf router, top-8; "
                      "16 distinct layers chained (residual + RMSNorm)",
          "tokens_per_s": round(T / (ms / 1e3), 1), "mean_active_experts": round(U, 2)}
-    r.update(rates(ms, nbytes, flops))
+    r.update(rates(ms, nbytes, flops, ffn=ffn_flops(T * K)))
     del arena
     return r, ws
 
@@ -240,7 +249,7 @@ def bench_prefill_down(torch, M, S, dev, stream, iters):
                                  out=out, flags=fl, ws=ws, stream=stream)
         ms = graph_time_ms(torch, one, stream, 3, iters) / L4
         r = {"tokens_per_s": round(T / (ms / 1e3), 1)}
-        r.update(rates(ms, nbytes, flops))
+        r.update(rates(ms, nbytes, flops, ffn=flops, split=not (fl & M.F_FP16_ACT)))
         res[name] = r
     del arena
     return res
@@ -276,7 +285,7 @@ def bench_prefill_stack(torch, M, S, dev, stream, arena, gates, iters):
          "tokens_per_s": round(T / (ms / 1e3), 1),
          "token_layers_per_s": round(T * L / (ms / 1e3), 1),
          "mean_active_experts": round(sum(Us) / len(Us), 2)}
-    r.update(rates(ms, nbytes, flops))
+    r.update(rates(ms, nbytes, flops, ffn=len(Us) * ffn_flops(MB * K)))
     r["ms_per_call"] = round(ms / len(Us), 5)
     r["ms_per_pass"] = round(ms, 4)
     del outs
