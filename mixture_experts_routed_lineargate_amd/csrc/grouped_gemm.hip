@@ -33,16 +33,21 @@
 // hi/lo fp16 pair for d*q would need three MFMAs per block in split mode and
 // twice the dequantisation work; the scaled form is 7-10% faster end to end.)
 //
-// K loop: chunks of 2 blocks (64 values).  Activation chunks go from global
-// memory straight into a ring of three LDS buffers (global_load_lds, 16-byte
-// pieces XOR-swizzled by row so fragment reads are conflict-free), two chunks
-// ahead, shared by the four wavefronts.  Weights never touch LDS: each lane loads
-// the dwords of its own fragment (the four lanes of a row read 12 + 8 bytes of
-// the row's two blocks) one chunk ahead, and the block scales come from the lanes
-// that hold them (ds_bpermute).  The weight loads are interleaved with the MFMAs
-// so that the texture-address unit, which spends about the same time on every
-// 64-lane load whatever its width, sees a steady stream instead of bursts.  A
-// tile whose rows fill fewer than four 16-row subtiles multiplies only those.
+// K loop: chunks of 2 blocks (64 values), both operands streamed from global
+// memory straight into LDS (global_load_lds, 16-byte pieces, no registers): the
+// activation chunk with its pieces XOR-swizzled by row (conflict-free fragment
+// reads), and the tile's 256 weight-row chunks, each copied as whole 16-byte
+// pieces into an 80-byte (Q8_0) or 48-byte (4-bit) LDS row from which every lane
+// reads its own fragment dwords and block scales.  Two buffers per operand: the
+// next chunk is requested while this one is multiplied, then one wait and one
+// barrier.  Vector-memory instructions are what bounds this kernel (the
+// texture-address unit spends about the same time on every 64-lane load whatever
+// its width), and 16-byte pieces need the fewest: per wavefront and chunk 4
+// activation and 5 (Q8_0) or 3 (4-bit) weight loads, against 8 weight loads when
+// each lane fetched its fragment dwords itself.  A tile whose rows fill fewer than
+// four 16-row subtiles multiplies only those.  expert_offsets and the per-expert
+// tile starts live in dynamic LDS sized to E, so that the Q8_0 form (77 KB) still
+// fits two workgroups per CU.
 #include "mfma_frag.hpp"
 
 namespace moe {
@@ -76,6 +81,43 @@ struct Args {
   float* y;                  // down: y [R][N] in flat order
 };
 
+// Weight rows of one K chunk staged in LDS by DMA: a row's chunk (68 / 36 bytes)
+// is copied as 16-byte pieces into an LDS row of ROWB bytes; the last piece is
+// taken to end exactly at the chunk's end (it overlaps the one before), so no
+// read passes the row.
+template <int FMT>
+struct LdsRow;
+template <>
+struct LdsRow<MOE_FMT_Q8_0> {
+  static constexpr int BB = 34, CB = 2 * BB;       // block bytes; bytes of a row's chunk
+  static constexpr int SLOTS = 5, ROWB = 80;
+  __device__ static uint32_t piece_off(int j) { return j < 4 ? 16u * j : 52u; }
+  // block 0 codes 8g .. 8g+7 (bytes 2+8g ..), block 1 codes (bytes 36+8g ..), scales
+  __device__ static void frag(const uint8_t* rb, int g, h8& q0, h8& q1, float& s0, float& s1) {
+    const uint32_t* w = (const uint32_t*)rb;
+    const uint32_t d0 = w[2 * g], d1 = w[2 * g + 1], d2 = w[2 * g + 2];
+    q0 = codes_q8(__builtin_amdgcn_alignbyte(d1, d0, 2), __builtin_amdgcn_alignbyte(d2, d1, 2));
+    const uint32_t e0 = w[9 + 2 * g];
+    const uint32_t e1 = g < 3 ? w[10 + 2 * g] : w[19];    // bytes 64..67 sit at 76 (last piece)
+    q1 = codes_q8(e0, e1);
+    s0 = half_lo(w[0]);
+    s1 = half_hi(w[8]);
+  }
+};
+template <>
+struct LdsRow<MOE_FMT_Q4> {
+  static constexpr int BB = 18, CB = 2 * BB;
+  static constexpr int SLOTS = 3, ROWB = 48;
+  __device__ static uint32_t piece_off(int j) { return j < 2 ? 16u * j : 20u; }
+  __device__ static void frag(const uint8_t* rb, int g, h8& q0, h8& q1, float& s0, float& s1) {
+    const uint32_t* w = (const uint32_t*)rb;
+    q0 = codes_q4(__builtin_amdgcn_alignbyte(w[g + 1], w[g], 2));
+    q1 = codes_q4(w[8 + g]);                                 // bytes 20+4g.. sit at 32+4g
+    s0 = half_lo(w[0]);
+    s1 = half_hi(w[4]);
+  }
+};
+
 __device__ inline int xcd_swizzle(int bid, int total) {
   // bid = 8 s + x runs on XCD x; give XCD x a contiguous range of tiles
   const int x = bid & 7, s = bid >> 3;
@@ -107,9 +149,8 @@ static int device_cus() {
 // into LDS in one batch, so the dependent index loads cost one round trip per
 // window rather than per tile.
 //
-// K pipeline: see the loop below (activations two chunks ahead in a ring of
-// three LDS buffers, weights one chunk ahead in registers, one barrier per
-// 64-value chunk).
+// K pipeline: see the loop below (both operands one chunk ahead in two LDS
+// buffers each, one wait and one barrier per 64-value chunk).
 //
 // Wavefront w computes 64 rows x 64 weight rows (4 x 4 MFMA tiles): down rows
 // 64w .. 64w+63, or gate rows 32w .. 32w+31 (subtiles 0, 1) and the up rows
@@ -118,7 +159,6 @@ static int device_cus() {
 // read touches fall in distinct banks.
 template <int FMT, int STAGE, int MSUB, bool SPLIT>
 __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
-  using FF = Fmt<FMT>;
   constexpr int BM = 16 * MSUB;
   constexpr int TW = NT / BM;                       // tiles per metadata window
   constexpr int PL = SPLIT ? 2 : 1;                 // activation planes
@@ -126,10 +166,13 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
   constexpr int A_DMA = BM * (BK / 8) >= NT ? BM * (BK / 8) / NT : 1;   // 16-byte loads / plane
   constexpr int A_SLOTS = BM * (BK / 8);            // 16-byte pieces of one plane of one chunk
   constexpr int BUF = PL * A_BYTES;
-  constexpr int NBUF = 3;                           // activation chunks in LDS
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * BUF];
-  __shared__ int offs[MAX_E + 1];                   // expert_offsets clamped to [0, R]
-  __shared__ int tstart[MAX_E + 1];                 // M-tiles of experts < e
+  using LR = LdsRow<FMT>;
+  constexpr int BBUF = BN * LR::ROWB;               // one chunk of the tile's weight rows
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsb[2 * BBUF];
+  extern __shared__ int dyn_lds[];                  // 2 (E + 1) ints, sized at launch
+  int* offs = dyn_lds;                              // expert_offsets clamped to [0, R]
+  int* tstart = dyn_lds + (p.E + 1);                // M-tiles of experts < e
   __shared__ int total_m;
   __shared__ int m_src[TW][BM];                     // activation row (always a valid row)
   __shared__ int m_flat[TW][BM];                    // flat row t*k+j, -1 = padding
@@ -165,7 +208,7 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
   const int G = gridDim.x;
   const int first = xcd_swizzle(blockIdx.x, G);
   const int ntiles = (total - first + G - 1) / G;
-  const int64_t RB = (int64_t)(p.K / QK) * FF::BB;  // bytes per stored weight row
+  const int64_t RB = (int64_t)(p.K / QK) * LR::BB;  // bytes per stored weight row
   const int nchunks = p.K / BK;                     // even (K is a multiple of 128)
 
   auto decode_tile = [&](int L, int& e, int& row0, int& nrows, int& nt) {
@@ -277,13 +320,19 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
         }
       };
 
-      // Weight dwords of one K chunk (two blocks) for the lane's row of each n-subtile,
-      // loaded straight into the fragment layout (lane group lg takes k = 8lg .. 8lg+7 of
-      // each block), plus the two dwords holding the block scales.
-      typename FF::Raw braw[4];
-      auto load_b = [&](int c) {
+      // Weight rows: wavefront w copies tile rows 64w .. 64w+63 (rows < BN/2 come
+      // from hb0, the rest from hb1), LR::SLOTS pieces per row.
+      const uint8_t* wbase = wave < 2 ? hb0 + (int64_t)(64 * wave) * RB : hb1 + (int64_t)(64 * (wave - 2)) * RB;
+      uint32_t boff[LR::SLOTS];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) FF::load(sb[s] + (int64_t)c * FF::CB, lrow, lg, braw[s]);
+      for (int i = 0; i < LR::SLOTS; ++i) {
+        const int q = 64 * i + lane;
+        boff[i] = (uint32_t)((q / LR::SLOTS) * RB) + LR::piece_off(q % LR::SLOTS);
+      }
+      auto load_b = [&](int c, uint8_t* bb) {
+#pragma unroll
+        for (int i = 0; i < LR::SLOTS; ++i)
+          lds_dma16(wbase + (int64_t)c * LR::CB, boff[i], bb + (64 * LR::SLOTS * wave + 64 * i) * 16);
       };
 
       // The K loop and epilogue of one tile whose rows fill MS 16-row subtiles.
@@ -297,8 +346,12 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
 
         // Per block: t = (a_hi [+ a_lo]) . q on the exact integer codes, then
         // acc += d * t with the block's fp16 scale d of the lane's column.
-        auto compute = [&](const uint8_t* buf, const h8 (&bq)[BKB][4], const float (&dsc)[BKB][4]) {
+        auto compute = [&](const uint8_t* buf, const uint8_t* bb) {
           const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          h8 bq[BKB][4];
+          float dsc[BKB][4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) LR::frag(bb + (wrow[s] + ln) * LR::ROWB, lg, bq[0][s], bq[1][s], dsc[0][s], dsc[1][s]);
 #pragma unroll
           for (int m = 0; m < MS; ++m) {
             h8 ah[BKB], al[BKB];
@@ -321,39 +374,22 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
           }
         };
 
-        // One chunk: decode this chunk's weights (the wait for them also covers the
-        // activation chunk requested before them: loads complete in issue order),
-        // request the activations two chunks ahead (into the LDS buffer freed by the
-        // previous chunk) and the weights one chunk ahead, multiply, one barrier
-        // (which publishes the next activation chunk to every wavefront).  Indices
-        // are clamped at the end, so every load is unconditional.
+        // One chunk: request the next chunk's activations and weights into the other
+        // buffers (freed by the previous chunk), multiply, wait for the requests,
+        // one barrier (which publishes them).
         load_a(0, lds);
-        load_a(min(1, nchunks - 1), lds + BUF);
-        load_b(0);
+        load_b(0, ldsb);
         __builtin_amdgcn_s_waitcnt(0x0f70);          // vmcnt(0)
         __syncthreads();
-        int bc = 0;                                   // buffer of chunk c
         for (int c = 0; c < nchunks; ++c) {
-          const uint8_t* cur = lds + bc * BUF;
-          const int b2 = bc == 0 ? 2 : bc - 1;        // buffer of chunk c + 2
-          h8 bq[BKB][4];
-          float dsc[BKB][4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) FF::decode(braw[s], ln, bq[0][s], bq[1][s], dsc[0][s], dsc[1][s]);
-          __builtin_amdgcn_sched_barrier(0);
-          load_a(min(c + 2, nchunks - 1), lds + b2 * BUF);
-          load_b(min(c + 1, nchunks - 1));
-          compute(cur, bq, dsc);
-          // spread the weight loads over the multiplies
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, MS * (SPLIT ? 2 : 1), 0);
-          }
+          const int bc = c & 1;
+          const int cn = min(c + 1, nchunks - 1);
+          load_a(cn, lds + (bc ^ 1) * BUF);
+          load_b(cn, ldsb + (bc ^ 1) * BBUF);
+          compute(lds + bc * BUF, ldsb + bc * BBUF);
+          __builtin_amdgcn_s_waitcnt(0x0f70);
           __syncthreads();
-          bc = bc == 2 ? 0 : bc + 1;
         }
-        __builtin_amdgcn_s_waitcnt(0x0f70);          // the clamped tail loads
 
         // ---- epilogue: lane holds rows 16m + 4*lg + i, column ln of each n-subtile ----
 #pragma unroll
@@ -403,7 +439,7 @@ static hipError_t launch_t(const Args& a, int64_t R, hipStream_t s) {
   if (cus <= 0) return hipErrorInvalidDevice;
   if (grid > (int64_t)cus * WG_PER_CU) grid = (int64_t)cus * WG_PER_CU;   // persistent
   hipLaunchKernelGGL((grouped_gemm_kernel<FMT, STAGE, MSUB, SPLIT>), dim3((unsigned)grid), dim3(NT),
-                     0, s, a);
+                     (size_t)2 * (a.E + 1) * sizeof(int), s, a);
   return hipGetLastError();
 }
 

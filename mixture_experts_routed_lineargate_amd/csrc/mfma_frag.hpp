@@ -2,10 +2,9 @@
 // (shared by the grouped GEMM kernels).  A lane of a B fragment holds the 8
 // weights k = 8g .. 8g+7 of one weight row within a 32-value block, as their
 // exact integer codes; the block's fp16 scale is applied to the MFMA result.
-// Two sources: frag_codes / frag_scale read a row staged in LDS through
-// `rd(off)` (the dword at byte offset `off`, a multiple of 4, of the stored
-// row); Fmt<FMT>::load / decode read one two-block chunk of a row straight from
-// global memory into the fragment layout.  lds_dma16 streams 16-byte pieces from
+// frag_codes / frag_scale read a row staged in LDS through `rd(off)` (the dword
+// at byte offset `off`, a multiple of 4, of the stored row); codes_q8 / codes_q4
+// turn code dwords into fp16 fragments; lds_dma16 streams 16-byte pieces from
 // global memory into LDS.
 #pragma once
 
@@ -95,69 +94,9 @@ __device__ inline float frag_scale(Rd rd, int b) {
   return (float)__builtin_bit_cast(_Float16, bits);
 }
 
-// One K chunk (two blocks) of a stored weight row, read straight into the MFMA
-// B-fragment layout: lane group g takes codes 8g .. 8g+7 of each block, plus the
-// dwords that hold the two block scales.  A chunk starts 4-byte aligned (rows
-// are whole 16-byte units and a chunk is 68 / 36 bytes), so block 0's codes sit
-// 2 bytes past a dword boundary and are realigned with alignbyte; block 1's are
-// dword aligned.
+// fp16 halves of a dword, as fp32
 __device__ inline float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ inline float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
-
-template <int FMT>
-struct Fmt;
-
-template <>
-struct Fmt<MOE_FMT_Q8_0> {
-  static constexpr int BB = 34;                // [d (fp16)][32 int8 codes]
-  static constexpr int CB = 2 * BB;             // 68 bytes per row per chunk: dwords D0 .. D16
-  struct Raw {
-    uint32_t c0[3];                            // D2g .. D2g+2: block 0 codes 8g .. 8g+7 at byte 2
-    uint32_t c1[2];                            // D9+2g, D10+2g: block 1 codes 8g .. 8g+7
-  };
-  // base: the chunk of the subtile's first row (uniform); lrow: byte offset of the
-  // lane's row from it
-  __device__ static void load(const uint8_t* base, uint32_t lrow, int g, Raw& r) {
-    const uint32_t* wg = (const uint32_t*)(base + (lrow + 8u * g));
-#pragma unroll
-    for (int i = 0; i < 3; ++i) r.c0[i] = wg[i];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) r.c1[i] = wg[9 + i];
-  }
-  // The scales sit in D0 (lane group 0's c0[0], low half) and D8 (lane group 3's
-  // c0[2], high half); ln is the lane's row within the subtile.
-  __device__ static void decode(const Raw& r, int ln, h8& q0, h8& q1, float& s0, float& s1) {
-    q0 = codes_q8(__builtin_amdgcn_alignbyte(r.c0[1], r.c0[0], 2),
-                  __builtin_amdgcn_alignbyte(r.c0[2], r.c0[1], 2));
-    q1 = codes_q8(r.c1[0], r.c1[1]);
-    s0 = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute(ln * 4, (int)r.c0[0]));
-    s1 = half_hi((uint32_t)__builtin_amdgcn_ds_bpermute((ln + 48) * 4, (int)r.c0[2]));
-  }
-};
-
-template <>
-struct Fmt<MOE_FMT_Q4> {
-  static constexpr int BB = 18;                // [d (fp16)][16 bytes of nibbles]
-  static constexpr int CB = 2 * BB;             // 36 bytes per row per chunk: dwords D0 .. D8
-  struct Raw {
-    uint32_t c0[2];                            // Dg, Dg+1: block 0 nibble bytes 4g .. 4g+3 at byte 2
-    uint32_t c1;                               // D5+g: block 1 nibble bytes 4g .. 4g+3
-  };
-  __device__ static void load(const uint8_t* base, uint32_t lrow, int g, Raw& r) {
-    const uint32_t* wg = (const uint32_t*)(base + (lrow + 4u * g));
-    r.c0[0] = wg[0];
-    r.c0[1] = wg[1];
-    r.c1 = wg[5];
-  }
-  // The scales sit in D0 (lane group 0's c0[0], low half) and D4 (lane group 3's
-  // c0[1], high half).
-  __device__ static void decode(const Raw& r, int ln, h8& q0, h8& q1, float& s0, float& s1) {
-    q0 = codes_q4(__builtin_amdgcn_alignbyte(r.c0[1], r.c0[0], 2));
-    q1 = codes_q4(r.c1);
-    s0 = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute(ln * 4, (int)r.c0[0]));
-    s1 = half_hi((uint32_t)__builtin_amdgcn_ds_bpermute((ln + 48) * 4, (int)r.c0[1]));
-  }
-};
 
 // global_load_lds_dwordx4: lane i of the wavefront writes the 16 bytes at
 // base + off (base wavefront-uniform, off a per-lane byte offset below 2^31) to
