@@ -243,7 +243,6 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
       wrow[s] = wave * 64 + s * 16;
   }
   const int ln = lane % 16, lg = lane / 16;
-  const uint32_t lrow = (uint32_t)(ln * RB);        // this lane's weight row within a subtile
 
   for (int k0 = 0; k0 < ntiles; k0 += TW) {
     // ---- metadata of the window's tiles ----
@@ -290,12 +289,6 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
         hb0 = p.w0 + (int64_t)e * p.s0 + (int64_t)n0 * RB;
         hb1 = hb0 + (int64_t)(BN / 2) * RB;
       }
-      // first weight row of n-subtile s (wavefront-uniform)
-      const uint8_t* sb[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sb[s] = wrow[s] < BN / 2 ? hb0 + (int64_t)wrow[s] * RB : hb1 + (int64_t)(wrow[s] - BN / 2) * RB;
-
       // activation 16-byte pieces of this thread: slot q = i*NT + tid (mod the slots of a
       // plane) is row q / 8, stored piece q % 8, holding logical piece (q % 8) ^ swz(row)
       uint32_t aoff[A_DMA];                           // byte offsets (planes are below 2 GiB)
@@ -308,6 +301,10 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
       // Activation chunk c goes straight from global memory into LDS buffer `buf`
       // (global_load_lds: lane i of a wavefront fills bytes 16i .. 16i+15 of the
       // wavefront's 1 KiB destination, so slot q = i*NT + tid lands at 16q).
+      // A wavefront's load i covers rows (i*NT + 64*wave) / 8 .. +7; loads that
+      // cover only rows past the last 16-row subtile holding rows are skipped
+      // (those rows are never multiplied).
+      const int arows = ((nrows + 15) / 16) * 16;
       auto load_a = [&](int c, uint8_t* buf) {
         if (A_SLOTS >= NT || wave * WAVE < A_SLOTS) {   // wavefront-uniform
 #pragma unroll
@@ -315,14 +312,16 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
             const _Float16* src = (pl ? p.alo : p.ahi) + c * BK;
 #pragma unroll
             for (int i = 0; i < A_DMA; ++i)
-              lds_dma16(src, aoff[i], buf + pl * A_BYTES + (i * NT + wave * WAVE) * 16);
+              if ((i * NT + wave * WAVE) / 8 < arows)       // wavefront-uniform
+                lds_dma16(src, aoff[i], buf + pl * A_BYTES + (i * NT + wave * WAVE) * 16);
           }
         }
       };
 
       // Weight rows: wavefront w copies tile rows 64w .. 64w+63 (rows < BN/2 come
-      // from hb0, the rest from hb1), LR::SLOTS pieces per row.
-      const uint8_t* wbase = wave < 2 ? hb0 + (int64_t)(64 * wave) * RB : hb1 + (int64_t)(64 * (wave - 2)) * RB;
+      // from hb0, the rest from hb1; BN/2 is a multiple of 64), LR::SLOTS pieces per row.
+      const uint8_t* wbase = 64 * wave < BN / 2 ? hb0 + (int64_t)(64 * wave) * RB
+                                                 : hb1 + (int64_t)(64 * wave - BN / 2) * RB;
       uint32_t boff[LR::SLOTS];
 #pragma unroll
       for (int i = 0; i < LR::SLOTS; ++i) {
