@@ -54,7 +54,7 @@ __global__ __launch_bounds__(NT, 1) void decode_layer_kernel(Args p) {
   __shared__ float red[NT];
   __shared__ float rsum[REPG];
   __shared__ __attribute__((aligned(16))) float lg[E];
-  __shared__ int top[K];
+  __shared__ __align__(16) int top[K];
   __shared__ int sel_e[K];
   __shared__ float sel_w[K];
 
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(NT, 1) void decode_layer_kernel(Args p) {
     }
     lg[lane] = v0;
     lg[lane + WAVE] = v1;
-    if (lane < K) top[lane] = lane;
+    if (lane < K) top[lane] = -1;
   }
   __syncthreads();
   select_top8_block(lg, top, sel_e, sel_w);

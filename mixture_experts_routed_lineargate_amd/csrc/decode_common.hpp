@@ -384,55 +384,79 @@ __device__ inline void load_dig(const uint8_t* dig, const float2* scl, int blk, 
 
 // Top-8 of E = 128 logits by rank counting, spread over the whole workgroup
 // (k rounds of a wave arg-max on one wavefront cost about 1.5 us per layer).
-// The caller has written lg[E] to LDS and set top[j] = j for j < K, followed
-// by a barrier.  Thread t (all NT = 4E threads) compares logit e = t / 4 with
-// logits 32*(t%4) .. +31; another logit outranks e if it is larger, or equal
-// with a lower index (the router's tie-break), so the ranks are a strict
-// total order and expert e is selected iff rank(e) < K.  Returns after a
-// barrier, with sel_e / sel_w holding the winners in ascending id and their
-// renormalised softmax weights.  Selected ids are in
-// [0, E) whatever the logits hold (NaN included).
+// Another logit outranks e if it is larger, or equal with a lower index (the
+// router's tie-break), so the ranks are a strict total order and expert e is
+// selected iff rank(e) < K.  The caller has written lg[E] to LDS and set
+// top[j] = -1 for j < K (top 16-byte aligned), followed by a barrier.
+// Thread t (all NT = 4E threads) compares logit e = t / 4 with logits
+// 32*(t%4) .. +31.  The first pass counts only the logits >= lg[e]; less one
+// (e itself) that is rank(e) whenever no other logit equals lg[e].  A group of
+// m >= 2 equal logits below c larger ones all land on slot c + m - 1 and
+// leave slot c empty, so when all K slots are filled no tie reaches the top K
+// and the slots hold the exact ranks (a NaN logit counts nothing and takes no
+// slot).  Otherwise a second pass ranks with the full comparison; every
+// slot is then preset to its own index, so the selected ids are in [0, E)
+// whatever the logits hold.  Returns after a barrier, with sel_e / sel_w
+// holding the winners in ascending id and their renormalised softmax weights.
 __device__ inline void select_top8_block(const float* lg, int* top, int* sel_e, float* sel_w) {
   static_assert(NT == 4 * E, "four threads per logit");
+  static_assert(K == 8, "the slots are read as two int4");
   const int tid = threadIdx.x;
   const int e = tid >> 2, q = tid & 3;
   const float le = lg[e];
-  // VALU-only counts: logits above le, and logits equal to le (itself included);
-  // the index tie-break runs only where le has an exact duplicate
-  int cnt = 0, eq = 0;
+  {
+    // every LDS read is issued before the first compare, so the reads overlap
+    float4 v[8];
 #pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    const float4 v = *(const float4*)(lg + 32 * q + i);
-    cnt += (v.x > le) + (v.y > le) + (v.z > le) + (v.w > le);
-    eq += (v.x == le) + (v.y == le) + (v.z == le) + (v.w == le);
+    for (int i = 0; i < 8; ++i) v[i] = *(const float4*)(lg + 32 * q + 4 * i);
+    int ge = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ge += (v[i].x >= le) + (v[i].y >= le) + (v[i].z >= le) + (v[i].w >= le);
+    ge += dpp<DPP_QUAD_1032>(ge);
+    ge += dpp<DPP_QUAD_2301>(ge);
+    if (q == 0 && ge >= 1 && ge <= K) top[ge - 1] = e;
   }
-  eq += dpp<DPP_QUAD_1032>(eq);
-  eq += dpp<DPP_QUAD_2301>(eq);
-  if (eq > 1) {
-#pragma unroll 1
-    for (int i = 0; i < 32; ++i) cnt += (lg[32 * q + i] == le) & (32 * q + i < e);
-  }
-  cnt += dpp<DPP_QUAD_1032>(cnt);
-  cnt += dpp<DPP_QUAD_2301>(cnt);
-  if (q == 0 && cnt < K) top[cnt] = e;
   __syncthreads();
+  int4 ta = *(const int4*)top, tb = *(const int4*)(top + 4);
+  if (min(min(min(ta.x, ta.y), min(ta.z, ta.w)), min(min(tb.x, tb.y), min(tb.z, tb.w))) < 0) {
+    // a slot is empty: exact ranks, with the index tie-break
+    __syncthreads();                                   // every thread has read the slots
+    if (tid < K) top[tid] = tid;
+    __syncthreads();
+    int cnt = 0;
+#pragma unroll 1
+    for (int i = 0; i < 32; ++i) {
+      const int o = 32 * q + i;
+      const float lo = lg[o];
+      cnt += (lo > le) | ((lo == le) & (o < e));
+    }
+    cnt += dpp<DPP_QUAD_1032>(cnt);
+    cnt += dpp<DPP_QUAD_2301>(cnt);
+    if (q == 0 && cnt < K) top[cnt] = e;
+    __syncthreads();
+    ta = *(const int4*)top;
+    tb = *(const int4*)(top + 4);
+  }
   if (tid < WAVE) {
-    // lane j < K takes winner j (rank order); the sum runs over the 8 lanes in a
-    // fixed tree order, so every workgroup gets the same bits
-    const int j = tid & (K - 1);
-    int ids[K];
+    // the slots are the same in every lane: lane j < K takes winner j (rank
+    // order); the sum runs over the 8 lanes in a fixed tree order, so every
+    // workgroup gets the same bits
+    int t[K] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-    for (int r = 0; r < K; ++r) ids[r] = min(max(top[r], 0), E - 1);
-    const int me = min(max(top[j], 0), E - 1);
-    const float ex = expf(lg[me] - lg[ids[0]]);
+    for (int r = 0; r < K; ++r) t[r] = __builtin_amdgcn_readfirstlane(min(max(t[r], 0), E - 1));
+    const int j = tid & (K - 1);
+    int me = t[0];
+#pragma unroll
+    for (int r = 1; r < K; ++r) me = j == r ? t[r] : me;
+    const float ex = __expf(lg[me] - lg[t[0]]);
     const float den = sum8(ex);
     int pos = 0;
 #pragma unroll
-    for (int r = 0; r < K; ++r) pos += ids[r] < me;
+    for (int r = 0; r < K; ++r) pos += t[r] < me;
     if (tid < K) {
       pos = min(pos, K - 1);
       sel_e[pos] = me;
-      sel_w[pos] = ex / den;
+      sel_w[pos] = ex * __builtin_amdgcn_rcpf(den);
     }
   }
   __syncthreads();

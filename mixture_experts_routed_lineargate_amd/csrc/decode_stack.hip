@@ -84,7 +84,7 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
   __shared__ float rsum[REPG];
   __shared__ float ssred[NWAVE];
   __shared__ __attribute__((aligned(16))) float lg[E];
-  __shared__ int top[K];
+  __shared__ __align__(16) int top[K];
   __shared__ int sel_e[K];
   __shared__ float sel_w[K];
   __shared__ float s_inv;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
       const float bm = lp.bias ? 1.f : 0.f;
       lg[lane] = fmaf(v0, inv, b0 * bm);
       lg[lane + WAVE] = fmaf(v1, inv, b1 * bm);
-      if (lane < K) top[lane] = lane;
+      if (lane < K) top[lane] = -1;
       if (lane == 0) s_inv = inv;
     } else {
       gather_fn<4>([=](int i) { return arep + tid + i * NT; }, t, p.err, budget, xo);

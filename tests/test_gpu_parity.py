@@ -87,22 +87,27 @@ def test_layer_parity(name, flags, request):
 
 
 @pytest.mark.parametrize("T", [1, 4])
-def test_exact_tie_at_the_boundary(decode_case, T):
+@pytest.mark.parametrize("rank", [7, 2])
+def test_exact_tie_at_the_boundary(decode_case, T, rank):
     """Two experts with the same gate column and bias get bit-identical logits; when
     they tie for 8th place the lower index is selected (the router's tie-break).  The
-    column of the 8th-ranked expert is copied onto the 9th, so the tied pair sits
-    above the old 10th by at least the case's 1e-3 gap and the rest of the
-    selection is unaffected.  T = 1 runs the fused single-token kernel and the decode
-    stack (one layer), T = 4 the router partials + top-k pass."""
+    column of the expert ranked `rank` (0-based) is copied onto the next one: at 7
+    the tied pair sits above the old 10th by at least the case's 1e-3 gap and the
+    rest of the selection is unaffected; at 2 both stay selected and only the
+    weights move.  T = 1 runs the fused single-token kernel and the decode stack
+    (one layer), T = 4 the router partials + top-k pass."""
     c = decode_case
     x = np.repeat(c.x[:1], T, axis=0)
     order = np.argsort(-O.router_logits(x[:1], c.G, c.b)[0], kind="stable")
-    e8, e9 = int(order[7]), int(order[8])
+    e8, e9 = int(order[rank]), int(order[rank + 1])
     G2, b2 = c.G.copy(), c.b.copy()
     G2[:, e9] = G2[:, e8]
     b2[e9] = b2[e8]
     r = O.moe_layer(x, G2, b2, c.oracle_experts(), c.k, residual=True)
-    assert min(e8, e9) in r["ids"][0] and max(e8, e9) not in r["ids"][0]
+    if rank == c.k - 1:
+        assert min(e8, e9) in r["ids"][0] and max(e8, e9) not in r["ids"][0]
+    else:
+        assert e8 in r["ids"][0] and e9 in r["ids"][0]
     tc = cases.Case(c.name, T, c.D, c.F, c.E, c.k, c.fmt, x=x, G=G2, b=b2, arena=c.arena)
     g = run_layer(tc, M.F_RESIDUAL)
     check_routing(g, r)
