@@ -41,7 +41,9 @@ constexpr int KMAX = 8;
 constexpr int TQ = TMAX * EMAX / NT;   // tokens per thread in R
 constexpr int QW = (NS_MAX * (EMAX + 1) + NT - 1) / NT;   // gathered words per thread in S
 static_assert(TMAX * SL % NT == 0 && SL * EMAX % NT == 0 && 2048 / 4 % NT == 0 && TMAX <= NT &&
-                  EMAX + 1 <= EP && TMAX * KMAX <= NT && TQ * (NT / EMAX) == TMAX, "shape");
+                  EMAX + 1 <= EP && TMAX * KMAX <= NT && TQ * (NT / EMAX) == TMAX && NT == 4 * EMAX &&
+                  EMAX == 2 * WAVE,
+              "shape");
 
 struct Args {
   const float* x;                   // [T][D]
@@ -67,8 +69,8 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
   __shared__ float gs[SL][EMAX];
   __shared__ float pl[NS_MAX * (EMAX + 1)];
   __shared__ float sums[EMAX + 1];
-  __shared__ float sel_l[4][MAX_K];
-  __shared__ int sel_e[4][MAX_K];
+  __shared__ __attribute__((aligned(16))) float lgt[EMAX];
+  __shared__ int top[KMAX];
   __shared__ int sids[KMAX];
   __shared__ int cnt[EMAX];
   __shared__ int base[EMAX];
@@ -170,20 +172,56 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
     }
     __syncthreads();
     const float inv = p.prenorm ? 1.0f / sqrtf(sums[E] / (float)D + PRENORM_EPS) : 1.0f;
+    // the top-k by rank counting over the workgroup (four threads a logit; k
+    // rounds of a wave arg-max on one wavefront cost ~3 us here): another logit
+    // outranks e if it is larger, or equal with a lower index, so expert e is
+    // selected iff fewer than k logits outrank it.  Slots start at their own
+    // index, so the ids are in [0, E) whatever the logits hold.
     if (wave == 0) {
-      float v[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int ee = i * WAVE + lane;
-        float l = -FLT_MAX;
+        float l = 0.f;
         if (ee < E) {
           l = sums[ee] * inv;
           if (p.bias) l += bv[i];
         }
-        v[i] = l;
+        lgt[ee] = l;
       }
-      select_and_write<2>(v, E, k, s, 0, lane, sel_l, sel_e, p.ids, p.w, sids);
+      if (lane < KMAX) top[lane] = lane;
       if (p.inv && lane == 0) p.inv[s] = inv;
+    }
+    __syncthreads();
+    {
+      const int e = tid >> 2, q = tid & 3;
+      int cnt = 0;
+      if (e < E) {
+        const float le = lgt[e];
+#pragma unroll 8
+        for (int i = 0; i < EMAX / 4; ++i) {
+          const int j = (EMAX / 4) * q + i;
+          const float lj = lgt[j];
+          cnt += (j < E) & ((lj > le) | ((lj == le) & (j < e)));
+        }
+      }
+      cnt += dpp<DPP_QUAD_1032>(cnt);
+      cnt += dpp<DPP_QUAD_2301>(cnt);
+      if (q == 0 && e < E && cnt < k) top[cnt] = e;
+    }
+    __syncthreads();
+    if (wave == 0 && lane < k) {
+      // renormalised softmax over the winners, summed in rank order; outputs in
+      // ascending id
+      const float lmax = lgt[min(max(top[0], 0), E - 1)];
+      float den = 0.f;
+      for (int r = 0; r < k; ++r) den += expf(lgt[min(max(top[r], 0), E - 1)] - lmax);
+      const int me = min(max(top[lane], 0), E - 1);
+      int rank = 0;
+      for (int r = 0; r < k; ++r) rank += top[r] < me;
+      rank = min(rank, k - 1);
+      p.ids[s * k + rank] = me;
+      sids[rank] = me;
+      p.w[s * k + rank] = expf(lgt[me] - lmax) / den;
     }
     // input planes of token s
 #pragma unroll
