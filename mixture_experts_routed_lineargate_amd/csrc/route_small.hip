@@ -7,8 +7,9 @@
 // (decode_common.hpp).  The arithmetic and its order are those of the separate
 // kernels: 64-row slices of d_model summed in slice order.
 //
-//  R  workgroup s (one per 64-row slice of d_model): partial logits of every
-//     token over the slice and the slice's sums of x^2; published.
+//  R  workgroup b: partial logits over slice s = b % NS (64 rows of d_model) of
+//     the tokens of group b / NS (8 tokens a group), and the slice's sums of
+//     x^2; published.
 //  S  workgroup t < T: gathers token t's partials and sums of squares, forms
 //     inv = 1/rms (with MOE_F_PRENORM, else 1), logits = inv * sum + bias, the
 //     top-k and renormalised weights (lower index wins ties), and the token's
@@ -19,7 +20,8 @@
 // Every word carries the launch's tag (launch counter + 1), so words of earlier
 // launches are never taken for this one.  The counter is advanced by workgroup 0
 // at its end: by then every workgroup has read it (workgroup 0 has seen every
-// slice's partials).  Every wait draws on a per-thread poll budget, so a launch
+// token's ids, and token t's workgroup had seen the partials of every slice of
+// t's group, so every workgroup had published).  Every wait draws on a per-thread poll budget, so a launch
 // always ends; a timeout sets the error word.
 #include "decode_common.hpp"
 #include "topk_select.hpp"
@@ -38,10 +40,11 @@ constexpr int TMAX = 32;            // tokens
 constexpr int EMAX = 128;           // experts (two logits per lane of one wavefront)
 constexpr int EP = 136;             // words per (slice, token): E partials, sum of squares at E
 constexpr int KMAX = 8;
-constexpr int TQ = TMAX * EMAX / NT;   // tokens per thread in R
+constexpr int TPG = 8;             // tokens per group in R (workgroups: slices x groups)
+constexpr int TQ = TPG * EMAX / NT;    // tokens per thread in R
 constexpr int QW = (NS_MAX * (EMAX + 1) + NT - 1) / NT;   // gathered words per thread in S
-static_assert(TMAX * SL % NT == 0 && SL * EMAX % NT == 0 && 2048 / 4 % NT == 0 && TMAX <= NT &&
-                  EMAX + 1 <= EP && TMAX * KMAX <= NT && TQ * (NT / EMAX) == TMAX && NT == 4 * EMAX &&
+static_assert(TPG * SL % NT == 0 && SL * EMAX % NT == 0 && 2048 / 4 % NT == 0 && TPG <= NT &&
+                  EMAX + 1 <= EP && TMAX * KMAX <= NT && TQ * (NT / EMAX) == TPG && NT == 4 * EMAX &&
                   EMAX == 2 * WAVE,
               "shape");
 
@@ -65,7 +68,7 @@ struct Args {
 };
 
 __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
-  __shared__ __attribute__((aligned(16))) float xs[TMAX][SL + 4];   // rows 16-byte aligned
+  __shared__ __attribute__((aligned(16))) float xs[TPG][SL + 4];    // rows 16-byte aligned
   __shared__ float gs[SL][EMAX];
   __shared__ float pl[NS_MAX * (EMAX + 1)];
   __shared__ float sums[EMAX + 1];
@@ -77,7 +80,8 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
   __shared__ int wcnt[NT / WAVE][EMAX];
 
   const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
-  const int s = blockIdx.x, ns = gridDim.x;
+  const int b = blockIdx.x, ns = p.D / SL;
+  const int s = b % ns, t0 = (b / ns) * TPG;     // R: slice, first token of the group
   const int T = p.T, D = p.D, E = p.E, k = p.k;
   uint32_t budget = SPIN_LIMIT;
   const uint32_t tg = __hip_atomic_load(p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
@@ -88,11 +92,11 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
 
   // ---- R: partial logits of slice s ----
   // (loads first, all unconditional: clamped rows and columns, masked at use)
-  constexpr int XL = TMAX * SL / NT;
+  constexpr int XL = TPG * SL / NT;
   float xv[XL];
 #pragma unroll
   for (int j = 0; j < XL; ++j) {
-    const int i = j * NT + tid, t = min(i / SL, T - 1), c = i % SL;
+    const int i = j * NT + tid, t = min(t0 + i / SL, T - 1), c = i % SL;
     xv[j] = p.x[(int64_t)t * D + s * SL + c];
   }
   constexpr int GL = SL * EMAX / NT;
@@ -102,11 +106,11 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
     const int i = j * NT + tid, c = i / EMAX, ee = i % EMAX;
     gv[j] = p.G[(int64_t)(s * SL + c) * E + min(ee, E - 1)];
   }
-  // token s's input row, needed in S only after the partials arrive
+  // token b's input row, needed in S only after the partials arrive
   constexpr int XR = 2048 / 4 / NT;
   float4 xr[XR];
   {
-    const int tt = min(s, T - 1);
+    const int tt = min(b, T - 1);
 #pragma unroll
     for (int j = 0; j < XR; ++j)
       xr[j] = *(const float4*)(p.x + (int64_t)tt * D + 4 * min(j * NT + tid, D / 4 - 1));
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
 #pragma unroll
   for (int j = 0; j < XL; ++j) {
     const int i = j * NT + tid;
-    xs[i / SL][i % SL] = i / SL < T ? xv[j] : 0.f;
+    xs[i / SL][i % SL] = t0 + i / SL < T ? xv[j] : 0.f;
   }
 #pragma unroll
   for (int j = 0; j < GL; ++j) {
@@ -140,24 +144,24 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
   }
 #pragma unroll
   for (int i = 0; i < TQ; ++i) {
-    const int t = th * TQ + i;
+    const int t = t0 + th * TQ + i;
     if (t < T && e < E) publish(p.xp + ((int64_t)s * TMAX + t) * EP + e, tg, acc[i]);
   }
-  if (tid < T) {
+  if (tid < TPG && t0 + tid < T) {
     float sq = 0.f;
 #pragma unroll
     for (int c = 0; c < SL; ++c) sq = fmaf(xs[tid][c], xs[tid][c], sq);
-    publish(p.xp + ((int64_t)s * TMAX + tid) * EP + E, tg, sq);
+    publish(p.xp + ((int64_t)s * TMAX + t0 + tid) * EP + E, tg, sq);
   }
 
-  // ---- S: token s ----
-  if (s < T) {
+  // ---- S: token b ----
+  if (b < T) {
     const int nw = ns * (E + 1);
     float vals[QW];
     gather_fn<QW>(
         [=](int i) {
           const int q = min(i * NT + tid, nw - 1);
-          return p.xp + ((int64_t)(q / (E + 1)) * TMAX + s) * EP + q % (E + 1);
+          return p.xp + ((int64_t)(q / (E + 1)) * TMAX + b) * EP + q % (E + 1);
         },
         tg, p.err, budget, vals);
 #pragma unroll
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
         lgt[ee] = l;
       }
       if (lane < KMAX) top[lane] = lane;
-      if (p.inv && lane == 0) p.inv[s] = inv;
+      if (p.inv && lane == 0) p.inv[b] = inv;
     }
     __syncthreads();
     {
@@ -219,11 +223,11 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
       int rank = 0;
       for (int r = 0; r < k; ++r) rank += top[r] < me;
       rank = min(rank, k - 1);
-      p.ids[s * k + rank] = me;
+      p.ids[b * k + rank] = me;
       sids[rank] = me;
-      p.w[s * k + rank] = expf(lgt[me] - lmax) / den;
+      p.w[b * k + rank] = expf(lgt[me] - lmax) / den;
     }
-    // input planes of token s
+    // input planes of token b
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
       const int d = 4 * (j * NT + tid);
@@ -232,16 +236,16 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const _Float16 hi = (_Float16)u[i];
-        p.xhi[(int64_t)s * D + d + i] = hi;
-        if (p.xlo) p.xlo[(int64_t)s * D + d + i] = (_Float16)(u[i] - (float)hi);
+        p.xhi[(int64_t)b * D + d + i] = hi;
+        if (p.xlo) p.xlo[(int64_t)b * D + d + i] = (_Float16)(u[i] - (float)hi);
       }
     }
     __syncthreads();                                  // sids written by wavefront 0
-    if (tid < k) publish(p.xi + s * KMAX + tid, tg, __int_as_float(sids[tid]));
+    if (tid < k) publish(p.xi + b * KMAX + tid, tg, __int_as_float(sids[tid]));
   }
 
   // ---- G: grouping of the T*k ids (workgroup 0) ----
-  if (s == 0) {
+  if (b == 0) {
     const int N = T * k;
     float idv[1];
     gather_fn<1>([=](int) { const int i = min(tid, N - 1); return p.xi + (i / k) * KMAX + i % k; },
@@ -333,7 +337,9 @@ hipError_t launch_route_small(const float* x, int64_t T, int D, const float* G, 
   static_assert(ROUTE_SYNC_OFF + (size_t)rs::NS_MAX * rs::TMAX * rs::EP * 8 +
                         (size_t)rs::TMAX * rs::KMAX * 8 <= SYNC_BYTES,
                 "sync region");
-  hipLaunchKernelGGL(rs::route_small_kernel, dim3((unsigned)(D / rs::SL)), dim3(rs::NT), 0, s, a);
+  const int groups = (int)((T + rs::TPG - 1) / rs::TPG);
+  hipLaunchKernelGGL(rs::route_small_kernel, dim3((unsigned)(D / rs::SL * groups)), dim3(rs::NT), 0, s,
+                     a);
   return hipGetLastError();
 }
 
