@@ -248,6 +248,7 @@ def test_prefill_layer_sampled_tokens():
     (37, 2048, 768, 128, 8, 1),   # ragged beyond a 32-token tile, 4-bit
     (3, 2048, 768, 128, 1, 0),    # top-1
     (17, 2048, 768, 64, 4, 0),    # odd small batch, 64 experts, top-4 (one-launch routing)
+    (9, 2048, 768, 128, 8, 1),    # one-launch routing: a full 8-token group and a 1-token group
     (32, 2048, 768, 100, 8, 1),   # 100 experts (one-launch routing, non-power-of-two grouping)
     (4, 96, 64, 1, 1, 1),         # one expert, top-1: a dense SwiGLU FFN
     (7, 64, 32, 6, 6, 0),         # every expert selected
