@@ -177,7 +177,7 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
     __syncthreads();
     const float inv = p.prenorm ? 1.0f / sqrtf(sums[E] / (float)D + PRENORM_EPS) : 1.0f;
     // the top-k by rank counting over the workgroup (four threads a logit; k
-    // rounds of a wave arg-max on one wavefront cost ~3 us here): another logit
+    // rounds of a wave arg-max on one wavefront took ~0.5 us longer): another logit
     // outranks e if it is larger, or equal with a lower index, so expert e is
     // selected iff fewer than k logits outrank it.  Slots start at their own
     // index, so the ids are in [0, E) whatever the logits hold.
