@@ -410,12 +410,84 @@ def pin_stack_zero_experts(O):
         cur = cur / np.sqrt((cur ** 2).mean(axis=1, keepdims=True) + 1e-6)
 
 
+def pin_stack_live_experts(O):
+    """Stacks of live layers against a torch float64 composition written out here:
+    o_1 = x + MoE_1(x), then in_{l+1} = rms_norm(o_l) and o_{l+1} = in_{l+1} + MoE_{l+1}(in_{l+1}).
+
+    Two stacks of three layers: one expert per layer with top-1 (MoE = that dense
+    SwiGLU FFN), and three experts per layer all selected (k = E, so MoE = sum_e
+    softmax(l)_e FFN_e with scipy's softmax).  Live experts make o_l differ from
+    in_l, so normalising the wrong vector, dropping the residual, normalising
+    before the first layer or skipping a norm all move the result."""
+    import torch
+    import torch.nn.functional as Fn
+    from scipy.special import softmax
+    rng = np.random.default_rng(17)
+    D, F_ = 64, 96
+    for E in (1, 3):
+        layers, dense_layers = [], []
+        for l in range(3):
+            fmt = (l + E) % 2
+            mats, dense = {}, []
+            for e in range(E):
+                Wg, rg = _exact_matrix(rng, D, F_, fmt)
+                Wu, ru = _exact_matrix(rng, D, F_, fmt)
+                Wd, rd = _exact_matrix(rng, F_, D, fmt)
+                mats[e] = (rg, ru, rd)
+                dense.append(tuple(torch.from_numpy(m) for m in (Wg, Wu, Wd)))
+            G = (rng.standard_normal((D, E)) * 0.3).astype(np.float32)
+            b = rng.standard_normal(E).astype(np.float32)
+            layers.append((G, b, _experts_from(mats, fmt, O)))
+            dense_layers.append((G, b, dense))
+        x0 = (rng.standard_normal((5, D)) * 2.0).astype(np.float32)
+        cur = torch.from_numpy(x0).double()
+        ins, outs = [], []
+        for l, (G, b, dense) in enumerate(dense_layers):
+            if l > 0:
+                cur = Fn.rms_norm(outs[-1], (D,), eps=1e-6)
+            p = softmax(cur.numpy() @ G.astype(np.float64) + b.astype(np.float64), axis=1)
+            mix = sum(torch.from_numpy(p[:, e:e + 1]) *
+                      ((Fn.silu(cur @ Wg) * (cur @ Wu)) @ Wd)
+                      for e, (Wg, Wu, Wd) in enumerate(dense))
+            ins.append(cur)
+            outs.append(cur + mix)
+        res = O.stack(x0, layers, E)
+        assert len(res) == 3
+        for l in range(3):
+            scale = float(outs[l].abs().max())
+            assert np.allclose(res[l]["out"], outs[l].numpy(), rtol=1e-12, atol=1e-12 * scale), (E, l)
+            assert np.allclose(res[l]["in"], ins[l].numpy(), rtol=1e-12, atol=1e-12), (E, l)
+        # the layers are live: o_l is far from in_l, so the recurrences differ
+        assert min(np.abs(r["out"] - r["in"]).max() for r in res) > 0.1
+
+
+def pin_topk_gap(O):
+    """The k-th minus (k+1)-th largest logit per row, against a Python sort of each
+    row (exact ties give a gap of 0; k = E gives +inf)."""
+    rng = np.random.default_rng(18)
+    for trial in range(200):
+        E = int(rng.integers(2, 12))
+        k = int(rng.integers(1, E + 1))
+        T = int(rng.integers(1, 5))
+        l = rng.standard_normal((T, E)) if trial % 2 else rng.integers(-2, 3, (T, E)).astype(float)
+        got = O.topk_gap(l, k)
+        assert got.shape == (T,)
+        for t in range(T):
+            s = sorted(l[t].tolist(), reverse=True)
+            want = math.inf if k == E else s[k - 1] - s[k]
+            assert got[t] == want, (l[t], k, got[t], want)
+    # a tie across the k-th / (k+1)-th boundary has no gap; a clear one has its size
+    assert O.topk_gap(np.array([[3.0, 1.0, 1.0, 0.0]]), 2)[0] == 0.0
+    assert O.topk_gap(np.array([[3.0, 1.0, 0.25, 0.0]]), 2)[0] == 0.75
+
+
 ALL_PINS = [
     pin_page_expert_size, pin_fp16_decoder, pin_q8_0_exhaustive, pin_q4_exhaustive,
     pin_matrix_orientation, pin_encoder_roundtrip, pin_topk_bruteforce, pin_tie_break_zero_gate,
     pin_weights_closed_form, pin_full_selection_is_softmax, pin_router_logits, pin_grouping,
     pin_dense_reduction, pin_all_experts_mixture, pin_zero_input, pin_scalar_bruteforce,
     pin_linearity, pin_equivariance, pin_down_combine, pin_rmsnorm, pin_stack_zero_experts,
+    pin_stack_live_experts, pin_topk_gap,
 ]
 
 

@@ -144,6 +144,30 @@ def _stack_no_residual(x0, layers, k, eps=1e-6, on_layer=None):
     return res
 
 
+def _stack_normalises_input(x0, layers, k, eps=1e-6, on_layer=None):
+    cur = np.asarray(x0, dtype=np.float64)
+    res = []
+    for l, (G, b, ex) in enumerate(layers):
+        if l > 0:
+            cur = O.rmsnorm(cur, eps)          # in_l instead of o_l
+        r = O.moe_layer(cur, G, b, ex, k, residual=True)
+        r["in"] = cur
+        res.append(r)
+    return res
+
+
+def _gap_vacuous(logits, k):
+    return np.full(np.asarray(logits).shape[0], np.inf)
+
+
+def _gap_off_by_one(logits, k):
+    T, E = logits.shape
+    s = -np.sort(-logits, axis=1)
+    if k + 1 >= E:
+        return np.full(T, np.inf)
+    return s[:, k] - s[:, k + 1]
+
+
 MUTATIONS = {
     "q4 nibble order swapped": ("decode_rows", _decode_nibbles_swapped),
     "q4 missing -8": ("decode_rows", _decode_no_offset),
@@ -163,6 +187,9 @@ MUTATIONS = {
     "expert fed the wrong token": ("expert_outputs", _expert_outputs_wrong_token),
     "expert size from the 4-bit format": ("expert_bytes", _expert_bytes_q4),
     "stack without residual": ("stack", _stack_no_residual),
+    "stack normalises in_l instead of o_l": ("stack", _stack_normalises_input),
+    "gap rule vacuous": ("topk_gap", _gap_vacuous),
+    "gap taken one rank too low": ("topk_gap", _gap_off_by_one),
 }
 
 
