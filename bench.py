@@ -331,9 +331,7 @@ def main():
         M.moe_decode_stack(x0[0], stack_layers, K, outs, ws=ws, stream=stream)
 
     ms_step = graph_time_ms(torch, one_stack, stream, a.warmup, a.steps)
-    err = int(ws[64:68].view(torch.int32).item())    # exchange-wait timeout flag
-    if err:
-        raise RuntimeError("decode kernel reported an exchange-wait timeout")
+    M.check_workspace(ws, stream=stream)             # raises if an exchange wait gave up
     if not torch.isfinite(outs).all():
         raise RuntimeError("non-finite output")
     print(f"[bench] decode stack: {ms_step * 1e3 / L:.2f} us per layer", file=sys.stderr, flush=True)
@@ -384,8 +382,7 @@ def main():
                             flags=flags if l > 0 else M.F_RESIDUAL, ws=ws, stream=stream)
 
         ms_pl = graph_time_ms(torch, one_pass, stream, a.warmup, a.steps)
-        if int(ws[64:68].view(torch.int32).item()):
-            raise RuntimeError("decode kernel reported an exchange-wait timeout")
+        M.check_workspace(ws, stream=stream)
         diff = float((bufs[L][0] - outs[L - 1]).abs().max() / outs[L - 1].pow(2).mean().sqrt())
         extra["decode_per_layer"] = {
             "workload": "the same 48-layer step as 48 moe_layer calls (decode_layer_kernel<Q8_0>)",

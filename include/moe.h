@@ -14,7 +14,8 @@
  *  - Pointers named in the signature are DEVICE pointers unless the comment
  *    says host.  fp32 arrays are row-major and 4-byte aligned.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
- *    stream).  No call synchronises with the host or copies device -> host, so
+ *    stream).  No call except moe_workspace_status (a diagnostic, documented
+ *    below) synchronises with the host or copies device -> host, so
  *    data-dependent sizes (per-expert counts) stay on the device and every
  *    call can be captured in a HIP graph.  The hidden state never re-enters
  *    the host between calls (technical-overview page, "Target boundary").
@@ -29,9 +30,19 @@
  *  - Errors: arguments are validated on the host before anything is enqueued;
  *    on an error the call returns a status != MOE_OK and enqueues nothing.
  *    MOE_E_HIP means a launch failed.  T == 0 is valid and enqueues nothing.
+ *  - Device-side errors: the fused kernels (single-token decode, decode stack,
+ *    small-batch routing) hand data between workgroups through tagged words
+ *    and need all their workgroups resident at once.  Every wait is bounded
+ *    (about a second of polling per launch); a wait that gives up sets the
+ *    u32 error word at byte 64 of the workspace to nonzero and returns NaN to
+ *    the code waiting on it, so the outputs that depend on it are NaN, never
+ *    stale data, and every launch still ends.  Causes: other work holding
+ *    compute units while a fused kernel runs, or a workspace that was not
+ *    zero-filled before first use.  Since the calls never synchronise, the
+ *    word is read with moe_workspace_status, which waits for the stream.
  *  - Data preconditions checked on the device rather than the host: expert ids
- *    outside [0, E) are dropped (the affected row contributes nothing and
- *    expert_offsets[E] ends below T*k).
+ *    outside [0, E) are dropped (the affected row contributes nothing to out,
+ *    its row of y is zero, and expert_offsets[E] ends below T*k).
  *
  * Block formats (weights are "native Q8_0", evidence page, GPU-native
  * foundation card; 4-bit experts: "Q4 expert execution", technical-overview
@@ -65,7 +76,9 @@ enum {
   MOE_E_FORMAT = 4,      /* unknown block format or stage                        */
   MOE_E_WORKSPACE = 5,   /* ws NULL or smaller than moe_workspace_bytes          */
   MOE_E_UNSUPPORTED = 6, /* limits: E > 1024, k > 32, D or F > 16384              */
-  MOE_E_HIP = 7          /* a HIP launch failed                                   */
+  MOE_E_HIP = 7,         /* a HIP launch failed                                   */
+  MOE_E_TIMEOUT = 8      /* moe_workspace_status: a fused kernel's bounded wait   */
+                         /* gave up since the word was last cleared               */
 };
 
 enum { MOE_FMT_Q8_0 = 0, MOE_FMT_Q4 = 1 };
@@ -121,7 +134,10 @@ size_t moe_workspace_bytes(int64_t T, int32_t D, int32_t F, int32_t E, int32_t k
  *     lower expert index, written in ascending id order.
  *   topk_w [T][k] fp32: softmax over all E logits, renormalised over the
  *     selected k (equal to the softmax of the selected logits); sums to 1.
- * Logits are accumulated in fp32. */
+ * Logits are accumulated in fp32.  A -inf logit (an expert masked by a -inf
+ * bias) ranks below every finite one and gets weight 0 when fewer than k are
+ * finite (ties among -inf go to the lower index).  NaN logits give
+ * unspecified ids, always within [0, E). */
 moe_status moe_route(const float* x, int64_t T, int32_t D, const float* gate, const float* bias,
                      int32_t E, int32_t k, int32_t* topk_ids, float* topk_w, void* ws,
                      size_t ws_bytes, void* stream);
@@ -217,6 +233,17 @@ moe_status moe_decode_stack(const float* x, int32_t num_layers,
 /* RMSNorm with unit gain (evidence page: "RMSNorm and residual transitions"):
  * out[t] = x[t] / sqrt(mean_D(x[t]^2) + eps).  out may equal x. */
 moe_status moe_rmsnorm(const float* x, int64_t T, int32_t D, float eps, float* out, void* stream);
+
+/* Device-side error word of a workspace (see "Device-side errors" above).
+ * SYNCHRONOUS: waits for every call enqueued on `stream` so far, then reads
+ * the u32 word at byte 64 of ws (a device pointer).  Returns MOE_OK if it is
+ * zero, MOE_E_TIMEOUT if a bounded wait of any call on this workspace gave up
+ * since it was last cleared (the outputs of that call hold NaN), MOE_E_HIP if
+ * the copy failed, MOE_E_NULLPTR / MOE_E_WORKSPACE for a missing or too small
+ * workspace (ws_bytes < 68).  With reset != 0 and a timeout recorded, the
+ * exchange region (the first 4 MiB, launch counters included) is zero-filled
+ * before returning, so the workspace is usable again.  Not for graph capture. */
+moe_status moe_workspace_status(void* ws, size_t ws_bytes, int32_t reset, void* stream);
 
 /* Host-side helpers. */
 const char* moe_status_str(moe_status s);

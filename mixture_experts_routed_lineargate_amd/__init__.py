@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_OK = 0
+MOE_E_TIMEOUT = 8
 FMT_Q8_0, FMT_Q4 = 0, 1
 STAGE_FULL, STAGE_DOWN = 0, 1
 F_RESIDUAL, F_DETERMINISTIC, F_PRENORM, F_FP16_ACT, F_BANDED = 1, 2, 4, 8, 16
@@ -57,6 +58,7 @@ _SIGS = {
     "moe_rmsnorm": (_I32, [_P, _I64, _I32, _F32, _P, _P]),
     "moe_decode_stack": (_I32, [_P, _I32, ctypes.POINTER(moe_stack_layer), _I32, _I32, _P, _P,
                                 _P, _P, _SZ, _P]),
+    "moe_workspace_status": (_I32, [_P, _SZ, _I32, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -213,6 +215,24 @@ def moe_layer(x, gate, bias, experts: Experts, k: int, out, flags: int = 0, topk
         _ptr(x), _ptr(gate), _ptr(bias), ctypes.byref(experts.c), T, k, flags, _ptr(out),
         _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_rows), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def moe_workspace_status(ws, reset: bool = False, stream=None) -> int:
+    """Status of the workspace's device-side error word (synchronous: waits for
+    ``stream``).  MOE_OK, or MOE_E_TIMEOUT when a fused kernel's bounded wait
+    gave up (its outputs hold NaN); ``reset`` zero-fills the exchange region
+    after a timeout so the workspace can be used again."""
+    import torch
+    _need(ws, torch.uint8, "ws")
+    return int(lib().moe_workspace_status(_ptr(ws), ws.numel(), 1 if reset else 0,
+                                          _stream(stream)))
+
+
+def check_workspace(ws, stream=None):
+    """Raise MoeError if a fused kernel's bounded wait gave up on this workspace."""
+    st = moe_workspace_status(ws, stream=stream)
+    if st != MOE_OK:
+        raise MoeError("moe_workspace_status", st)
 
 
 def moe_rmsnorm(x, out, eps: float = 1e-6, stream=None):

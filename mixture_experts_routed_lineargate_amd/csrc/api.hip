@@ -144,7 +144,12 @@ static moe_status do_ffn(const float* in, int stage, const ExpertsDev& W, const 
     else
       HIP_TRY(launch_grouped_down(hhi, hlo, a_mode, W, offsets, rows, R, k, ybuf, split, s,
                                   (flags & MOE_F_BANDED) != 0));
-    if (out) HIP_TRY(launch_combine(ybuf, w, T, k, W.D, res, out, s, res_scale));
+    // the grouped kernels write only the rows the grouping kept: the combine skips
+    // dropped entries (ids outside [0, E)) and sets their rows of the caller's y to 0
+    if (out)
+      HIP_TRY(launch_combine(ybuf, w, T, k, W.D, res, out, s, res_scale, ids, W.E, y));
+    else
+      HIP_TRY(launch_zero_dropped(ids, R, W.E, W.D, y, s));
     return MOE_OK;
   }
   const char* path = full ? "ffn generic gate/up+down" : "ffn generic down";
@@ -242,6 +247,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_E_WORKSPACE: return "workspace missing or too small";
     case MOE_E_UNSUPPORTED: return "shape outside supported limits";
     case MOE_E_HIP: return "HIP launch failed";
+    case MOE_E_TIMEOUT: return "a bounded exchange wait gave up (outputs hold NaN)";
     default: return "unknown status";
   }
 }
@@ -410,6 +416,26 @@ moe_status moe_decode_stack(const float* x, int32_t num_layers, const moe_stack_
                        topk_w ? topk_w + (size_t)l * k : nullptr, nullptr, nullptr, ws, s));
   }
   return MOE_OK;
+}
+
+moe_status moe_workspace_status(void* ws, size_t ws_bytes, int32_t reset, void* stream) {
+  if (!ws) return MOE_E_NULLPTR;
+  if (ws_bytes < ERR_WORD_OFF + sizeof(uint32_t)) return MOE_E_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t word = 0;
+  char* base = (char*)ws;
+  if (hipMemcpyAsync(&word, base + ERR_WORD_OFF, sizeof(word), hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MOE_E_HIP;
+  if (word == 0) return MOE_OK;
+  if (reset) {
+    // the launch counters may disagree after a timeout: zero the whole exchange region
+    const size_t n = ws_bytes < SYNC_BYTES ? ws_bytes : SYNC_BYTES;
+    if (hipMemsetAsync(ws, 0, n, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+      return MOE_E_HIP;
+  }
+  return MOE_E_TIMEOUT;
 }
 
 moe_status moe_rmsnorm(const float* x, int64_t T, int32_t D, float eps, float* out, void* stream) {

@@ -317,7 +317,7 @@ hipError_t launch_decode_fused(const float* x, const float* gate, const float* b
   a.rows = rows;
   // exchange buffers live in the workspace's sync region
   char* sync = (char*)ws.sync;
-  a.err = ws.sync + 16;                                   // byte 64
+  a.err = ws.sync + ERR_WORD_OFF / sizeof(uint32_t);
   a.epochs = (uint32_t*)(sync + 4096);                    // [256] u32
   a.part = (uint64_t*)(sync + 65536);                     // [32][8][128] u64 (256 KiB)
   a.h = (uint64_t*)(sync + 327680);                       // [4][8][768] u64 (192 KiB)

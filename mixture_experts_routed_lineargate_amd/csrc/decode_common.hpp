@@ -109,10 +109,15 @@ __device__ inline void repoll(uint64_t* v, AddrFn addr) {
 }
 
 // Finish a wait on N tagged words whose first reads are already in v: poll
-// (word i lives at addr(i)) until all carry tag t, then return the values.  Spends at most `budget` rounds (shared by every wait of the launch).
+// (word i lives at addr(i)) until all carry tag t, then return the values.
+// Spends at most `budget` rounds (shared by every wait of the launch).  A wait
+// that runs out of budget sets the error word and returns NaN for every word,
+// so whatever it feeds (logits, weights, h, outputs) is NaN, never stale data;
+// the selections clamp their ids into [0, E), so addressing stays in bounds.
 template <int N, typename AddrFn>
 __device__ inline void gather_finish(uint64_t* v, AddrFn addr, uint32_t t, uint32_t* err,
                                      uint32_t& budget, float* out) {
+  bool timed_out = false;
   for (;;) {
     bool ready = true;
 #pragma unroll
@@ -120,6 +125,7 @@ __device__ inline void gather_finish(uint64_t* v, AddrFn addr, uint32_t t, uint3
     if (ready) break;
     if (budget == 0) {
       __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      timed_out = true;
       break;
     }
     --budget;
@@ -127,7 +133,8 @@ __device__ inline void gather_finish(uint64_t* v, AddrFn addr, uint32_t t, uint3
     repoll<0, N>(v, addr);
   }
 #pragma unroll
-  for (int i = 0; i < N; ++i) out[i] = __uint_as_float((uint32_t)v[i]);
+  for (int i = 0; i < N; ++i)
+    out[i] = timed_out ? __builtin_nanf("") : __uint_as_float((uint32_t)v[i]);
 }
 
 // Wait until the N tagged words at addr(i) all carry tag t; all N loads of a

@@ -402,7 +402,7 @@ hipError_t launch_decode_stack(const float* x, int L, const StackLayer* layers, 
   a.ids = ids;
   a.w = w;
   char* sync = (char*)ws.sync;
-  a.err = ws.sync + 16;                                   // byte 64
+  a.err = ws.sync + ERR_WORD_OFF / sizeof(uint32_t);
   a.epochs = (uint32_t*)(sync + 4096);                    // [256] u32, shared with the layer kernel
   a.xb = (uint64_t*)(sync + 65536);                       // [32][8][136] u64 (272 KiB)
   a.xc = (uint64_t*)(sync + 65536 + 278528);              // [4][8][768] u64 (192 KiB)

@@ -112,9 +112,15 @@ hipError_t launch_down_generic(const float* h, const ExpertsDev& W, const int32_
 // out[t][d] = sum_j w[t][j] * y[t*k+j][d] (j ascending) (+ residual[t][d]).
 // Four outputs per thread when every row is 16-byte aligned (D % 4 == 0 and
 // aligned bases), one otherwise; the summation order is the same either way.
+// With ids, a slot whose expert id is outside [0, E) was dropped by the
+// grouping: its y row was never computed, so it is skipped, and when y_out is
+// given its row there is set to zero (the value the header promises for a
+// dropped entry).
 template <int V>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
-                                                      const float* __restrict__ w, int64_t T,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ ids, int E,
+                                                      float* __restrict__ y_out, int64_t T,
                                                       int k, int D,
                                                       const float* __restrict__ residual,
                                                       const float* __restrict__ res_scale,
@@ -124,8 +130,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (d >= D) return;
   float s[V] = {};
   for (int j = 0; j < k; ++j) {
-    const float wj = w[t * k + j];
-    const float* yr = y + (t * k + j) * D + d;
+    const int64_t r = t * k + j;
+    if (ids && (unsigned)ids[r] >= (unsigned)E) {
+      if (y_out) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) y_out[r * D + d + i] = 0.f;
+      }
+      continue;
+    }
+    const float wj = w[r];
+    const float* yr = y + r * D + d;
     if constexpr (V == 4) {
       const float4 v = *(const float4*)yr;
       s[0] = fmaf(wj, v.x, s[0]);
@@ -149,15 +163,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int D,
                           const float* residual, float* out, hipStream_t s,
-                          const float* res_scale) {
+                          const float* res_scale, const int32_t* ids, int E, float* y_out) {
   auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
-  if (D % 4 == 0 && a16(y) && a16(out) && a16(residual)) {
+  if (D % 4 == 0 && a16(y) && a16(out) && a16(residual) && a16(y_out)) {
     dim3 grid((unsigned)T, (unsigned)((D / 4 + 255) / 256));
-    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, s, y, w, T, k, D, residual, res_scale, out);
+    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, s, y, w, ids, E, y_out, T, k, D,
+                       residual, res_scale, out);
   } else {
     dim3 grid((unsigned)T, (unsigned)((D + 255) / 256));
-    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, s, y, w, T, k, D, residual, res_scale, out);
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, s, y, w, ids, E, y_out, T, k, D,
+                       residual, res_scale, out);
   }
+  return hipGetLastError();
+}
+
+// y[r] = 0 for every flat row r whose expert id is outside [0, E) (rows the
+// grouping dropped, which the grouped kernels never write).
+__global__ __launch_bounds__(256) void zero_dropped_kernel(const int32_t* __restrict__ ids,
+                                                           int64_t R, int E, int D,
+                                                           float* __restrict__ y) {
+  const int64_t r = blockIdx.x;
+  if ((unsigned)ids[r] < (unsigned)E) return;
+  for (int d = threadIdx.x; d < D; d += 256) y[r * D + d] = 0.f;
+}
+
+hipError_t launch_zero_dropped(const int32_t* ids, int64_t R, int E, int D, float* y,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(zero_dropped_kernel, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, D, y);
   return hipGetLastError();
 }
 

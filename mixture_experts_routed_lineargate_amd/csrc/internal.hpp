@@ -115,6 +115,7 @@ int router_ksplit(int64_t T, int D);
 Workspace carve_workspace(void* base, int64_t T, int D, int F, int E, int k, int flags);
 constexpr size_t SYNC_BYTES = 4 * 1024 * 1024;  // barrier words and exchange buffers
 constexpr size_t ROUTE_SYNC_OFF = 2 * 1024 * 1024;  // small-batch routing's exchange words
+constexpr size_t ERR_WORD_OFF = 64;                 // u32 error word (bounded wait gave up)
 
 bool trace_enabled();
 void trace(const char* what, int64_t T, int D, int F, int E, int k, int fmt);
@@ -149,10 +150,15 @@ hipError_t launch_gateup_generic(const float* x, const ExpertsDev& W, const int3
                                  int k, float* h, hipStream_t s);
 hipError_t launch_down_generic(const float* h, const ExpertsDev& W, const int32_t* ids, int64_t T,
                                int k, float* y, hipStream_t s);
-// residual row t is scaled by res_scale[t] when res_scale is given
+// residual row t is scaled by res_scale[t] when res_scale is given; with ids,
+// slots whose id is outside [0, E) are skipped (and their y_out rows zeroed)
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int D,
                           const float* residual, float* out, hipStream_t s,
-                          const float* res_scale = nullptr);
+                          const float* res_scale = nullptr, const int32_t* ids = nullptr,
+                          int E = 0, float* y_out = nullptr);
+// y rows of dropped entries (expert id outside [0, E)) set to zero
+hipError_t launch_zero_dropped(const int32_t* ids, int64_t R, int E, int D, float* y,
+                               hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, int64_t T, int D, float eps, float* out, hipStream_t s);
 
 // grouped GEMM on MFMA (batched / prefill expert FFN)

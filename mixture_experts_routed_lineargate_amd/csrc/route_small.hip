@@ -330,7 +330,7 @@ hipError_t launch_route_small(const float* x, int64_t T, int D, const float* G, 
   a.rows = rows;
   // exchange words in the workspace's sync region, clear of the decode kernels' regions
   char* sync = (char*)ws.sync;
-  a.err = ws.sync + 16;                                   // byte 64
+  a.err = ws.sync + ERR_WORD_OFF / sizeof(uint32_t);
   a.epoch = (uint32_t*)(sync + 8192);
   a.xp = (uint64_t*)(sync + ROUTE_SYNC_OFF);
   a.xi = (uint64_t*)(sync + ROUTE_SYNC_OFF + (size_t)rs::NS_MAX * rs::TMAX * rs::EP * 8);

@@ -10,6 +10,8 @@ oracle reads back the bytes of the experts it needs.
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -17,6 +19,27 @@ import moe_synth as S
 from oracle import moe_oracle as O
 
 GAP = 1e-3
+_POOL = None
+
+
+def pool():
+    """Threads for decoding experts in parallel (numpy releases the GIL in the
+    decode); at most 16, the CPU share of one GPU."""
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0)))))
+    return _POOL
+
+
+def layer_experts(arena_l, D, F, fmt, experts=None):
+    """The oracle's Experts for one layer's device arena [E][stride]: the bytes are
+    copied to the host once, and the experts named in ``experts`` (all when None)
+    are decoded up front by the oracle's own decoder on several threads."""
+    host = arena_l.cpu().numpy()
+    ex = O.Experts(lambda e: S.split_blob(host[e], D, F, fmt), fmt)
+    todo = range(host.shape[0]) if experts is None else sorted(set(int(e) for e in experts))
+    list(pool().map(ex.weights, todo))
+    return ex
 
 
 @dataclasses.dataclass
@@ -42,7 +65,11 @@ class Case:
         blob = self.arena[e].cpu().numpy()
         return S.split_blob(blob, self.D, self.F, self.fmt)
 
-    def oracle_experts(self):
+    def oracle_experts(self, prefetch=None):
+        """The oracle's view of the case's experts; ``prefetch`` = expert ids to
+        decode up front in parallel (large layers)."""
+        if prefetch is not None:
+            return layer_experts(self.arena, self.D, self.F, self.fmt, prefetch)
         return O.Experts(self.fetch, self.fmt)
 
 
@@ -106,16 +133,60 @@ def stack_layers(cfg, L, E, D, k):
 
 
 def stack_oracle(x_rows, gates, arena, D, F, k, fmt):
-    """Oracle trajectory of a few token rows through every layer of the stack.
+    """Oracle trajectory of token rows through every layer of the stack.
 
     Tokens are independent (no attention), so the trajectory of a token does not
-    depend on which other tokens share its microbatch.  Returns the per-layer
-    oracle results (``out`` = o_l, ``logits``, ``ids``)."""
+    depend on which other tokens share its microbatch.  Each layer's experts are
+    decoded up front on several threads (the oracle's own decoder; only the
+    bytes' path into it is the harness's).  Returns the per-layer oracle results
+    (``out`` = o_l, ``in`` = in_l, ``logits``, ``ids``, ``w``)."""
     def layers():
         for l, (G, b) in enumerate(gates):
-            fetch = (lambda e, l=l: S.split_blob(arena[l, e].cpu().numpy(), D, F, fmt))
-            yield G, b, O.Experts(fetch, fmt)
+            yield G, b, layer_experts(arena[l], D, F, fmt)
+
     def progress(l, r):
         if l % 8 == 7:
             print(f"  oracle: layer {l + 1}/{len(gates)} done", flush=True)
     return O.stack(x_rows, layers(), k, on_layer=progress)
+
+
+def redraw_along_trajectory(x0, rows, cfg, gates, arena, D, F, k, fmt, n_alt=3, max_rounds=6):
+    """Gap rule along the whole stack: redraw x0's rows (in place) until every
+    layer of each row's fp64 trajectory keeps the k-th/(k+1)-th logit gap >= GAP.
+
+    Row r's draws are x0[r] (attempt 0) then ``S.redraw_row(cfg, r, a, D)`` for
+    a = 1, 2, ... (its own sub-seed stream); the row keeps its first draw whose
+    trajectory holds the rule, which is what redrawing one attempt at a time
+    would give.  Each round evaluates the next n_alt + 1 attempts of every
+    pending row in one pass over the stack.  Returns ({row: oracle per-layer
+    results of the kept draw}, {row: attempts used})."""
+    rows = [int(r) for r in rows]
+    ref, used = {}, {}
+    pending = {r: 0 for r in rows}          # row -> first attempt of this round
+    for _ in range(max_rounds):
+        if not pending:
+            break
+        cand, who = [], []
+        for r, a0 in pending.items():
+            for a in range(a0, a0 + n_alt + 1):
+                cand.append(x0[r] if a == 0 else S.redraw_row(cfg, r, a, D))
+                who.append((r, a))
+        res = stack_oracle(np.stack(cand).astype(np.float32), gates, arena, D, F, k, fmt)
+        gap = np.min([O.topk_gap(l["logits"], k) for l in res], axis=0)
+        nxt = {}
+        for r, a0 in pending.items():
+            ok = [i for i, (rr, a) in enumerate(who) if rr == r and gap[i] >= GAP]
+            if ok:
+                i = min(ok, key=lambda i: who[i][1])
+                a = who[i][1]
+                if a > 0:
+                    x0[r] = S.redraw_row(cfg, r, a, D)
+                ref[r] = [{key: l[key][i] for key in ("out", "in", "ids", "w", "logits")}
+                          for l in res]
+                used[r] = a
+            else:
+                nxt[r] = a0 + n_alt + 1
+        pending = nxt
+    if pending:
+        raise RuntimeError(f"rows {sorted(pending)}: no draw keeps the gap rule")
+    return ref, used

@@ -34,9 +34,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(8):
-        assert M.status_str(s)
+    for s in range(9):
+        assert M.status_str(s) != "unknown status"
     assert M.status_str(0) == "ok"
+    assert M.status_str(9) == "unknown status"
 
 
 def test_workspace_bytes():
@@ -121,6 +122,12 @@ def test_expert_ffn_validation():
     down_only = _experts(w_gate=None, w_up=None)
     assert L.moe_expert_ffn(FAKE, 0, ctypes.byref(down_only), FAKE, FAKE, FAKE, FAKE, 4, 8, FAKE,
                             None, 0, FAKE, 1 << 40, None) == 1
+
+
+def test_workspace_status_validation():
+    L = M.lib()
+    assert L.moe_workspace_status(None, 1 << 20, 0, None) == 1
+    assert L.moe_workspace_status(FAKE, 67, 0, None) == 5
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import cases
+import margins
 import mixture_experts_routed_lineargate_amd as M
 import moe_synth as S
 from oracle import moe_oracle as O
@@ -47,7 +48,7 @@ def run_stack(x, dG, ex, flags, ws):
     M.moe_decode_stack(torch.from_numpy(x).to(DEV), layers, K, outs, flags=flags, topk_ids=ids,
                        topk_w=w, ws=ws)
     torch.cuda.synchronize()
-    assert int(ws[64:68].view(torch.int32).item()) == 0, "exchange-wait timeout"
+    M.check_workspace(ws)
     return outs.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
 
 
@@ -59,6 +60,7 @@ def check_trajectory(ref, t, outs, ids, w):
         err = rel_max_err(outs[l][None], r["out"][t][None])
         worst = max(worst, err)
         assert err <= TOL, f"layer {l}: max|d|/rms = {err:.3e}"
+    margins.record(f"token {t} through {len(ref)} layers", worst)
     return worst
 
 
