@@ -199,6 +199,29 @@ moe_status moe_layer(const float* x, const float* gate, const float* bias,
                      float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
                      int32_t* sorted_rows, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and kernels as moe_layer, with the workspace replaced by a static
+ * 8 MiB device array inside the library (one per GPU, held until the process
+ * ends).  The call allocates nothing and calls no allocating routine; the
+ * caller still passes inputs and outputs, as for moe_layer.
+ *  - Limit: moe_workspace_bytes(T, D, F, E, k, format, flags) must be at most
+ *    8 MiB (8,388,608 bytes): at d_model 2048, d_ff 768, 128 experts, top-8
+ *    that is T <= 34 tokens with MOE_F_PRENORM, T <= 36 without.  Larger calls
+ *    return MOE_E_UNSUPPORTED and enqueue nothing.
+ *  - Every call on a GPU shares that GPU's array, which keeps the last call's
+ *    contents: calls that may overlap on one GPU (concurrent streams, several
+ *    host threads) race and must be ordered by the caller.
+ *  - The first call on a device enqueues a zero fill of the array's exchange
+ *    region ahead of its own work on `stream`.
+ *  - A fused kernel's exchange wait that gives up makes the outputs NaN, as in
+ *    moe_layer; the error word sits in the library's array and is not readable
+ *    through moe_workspace_status. */
+moe_status moe_layer_noalloc(const float* x, const float* gate, const float* bias,
+                             const moe_experts* W /* host */, int64_t T, int32_t k, int32_t flags,
+                             float* out, int32_t* topk_ids, float* topk_w,
+                             int32_t* expert_offsets, int32_t* sorted_rows, void* stream);
+
 /* One layer of a decode stack (host struct holding device pointers). */
 typedef struct {
   const float* gate;   /* [D][E] fp32 LinearGate matrix */

@@ -59,6 +59,8 @@ _SIGS = {
     "moe_decode_stack": (_I32, [_P, _I32, ctypes.POINTER(moe_stack_layer), _I32, _I32, _P, _P,
                                 _P, _P, _SZ, _P]),
     "moe_workspace_status": (_I32, [_P, _SZ, _I32, _P]),
+    "moe_layer_noalloc": (_I32, [_P, _P, _P, ctypes.POINTER(moe_experts), _I64, _I32, _I32, _P, _P,
+                                 _P, _P, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -233,6 +235,23 @@ def check_workspace(ws, stream=None):
     st = moe_workspace_status(ws, stream=stream)
     if st != MOE_OK:
         raise MoeError("moe_workspace_status", st)
+
+
+def moe_layer_noalloc(x, gate, bias, experts: Experts, k: int, out, flags: int = 0,
+                      topk_ids=None, topk_w=None, expert_offsets=None, sorted_rows=None,
+                      stream=None):
+    """moe_layer with the library's static workspace (no allocation; see moe.h)."""
+    import torch
+    for t, dt, n in ((x, torch.float32, "x"), (gate, torch.float32, "gate"),
+                     (bias, torch.float32, "bias"), (out, torch.float32, "out"),
+                     (topk_ids, torch.int32, "topk_ids"), (topk_w, torch.float32, "topk_w"),
+                     (expert_offsets, torch.int32, "offsets"),
+                     (sorted_rows, torch.int32, "sorted_rows")):
+        _need(t, dt, n)
+    T = x.shape[0]
+    _check("moe_layer_noalloc", lib().moe_layer_noalloc(
+        _ptr(x), _ptr(gate), _ptr(bias), ctypes.byref(experts.c), T, k, flags, _ptr(out),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_rows), _stream(stream)))
 
 
 def moe_rmsnorm(x, out, eps: float = 1e-6, stream=None):

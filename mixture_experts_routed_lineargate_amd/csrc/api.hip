@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace moe {
@@ -229,6 +231,44 @@ static moe_status layer_impl(const float* x, const float* gate, const float* bia
                 flags & (MOE_F_RESIDUAL | MOE_F_DETERMINISTIC | MOE_F_FP16_ACT | MOE_F_BANDED), w, s);
 }
 
+// ---- the allocation-free variant of moe_layer ----
+// Its workspace is this file-scope device array (one copy per GPU, held until the
+// process ends).  In host code `scratch` names a host-side stand-in, not a device
+// address: the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that pointer is used from then on.
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+static void* scratch_dev[64];            // per-device address of `scratch`
+static std::mutex scratch_mu;
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The device address of the current device's scratch array.  The first call on a
+// device looks it up and enqueues, on `s` ahead of the caller's work, a zero fill of
+// the exchange region (launch counters and tagged words must start at zero); a
+// fill kernel rather than a memset, so that a call captured in a graph replays it
+// correctly.
+static moe_status scratch_for_device(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_E_HIP;
+  if (dev < 0 || dev >= 64) return MOE_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_E_HIP;
+    static_assert(SYNC_BYTES % 16 == 0 && SYNC_BYTES <= NOALLOC_SCRATCH_BYTES, "fill size");
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(256), dim3(256), 0, s, (uint4*)p,
+                       (size_t)SYNC_BYTES / 16);
+    if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -350,6 +390,33 @@ moe_status moe_layer(const float* x, const float* gate, const float* bias, const
   if (!ws || ws_bytes < need) return MOE_E_WORKSPACE;
   return layer_impl(x, gate, bias, W, T, k, flags, out, topk_ids, topk_w, expert_offsets,
                     sorted_rows, ws, (hipStream_t)stream);
+}
+
+moe_status moe_layer_noalloc(const float* x, const float* gate, const float* bias,
+                             const moe_experts* W, int64_t T, int32_t k, int32_t flags, float* out,
+                             int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                             int32_t* sorted_rows, void* stream) {
+  MOE_TRY(check_experts(W));
+  MOE_TRY(check_gate_up(W));
+  const int D = W->d_model, F = W->d_ff, E = W->num_experts;
+  MOE_TRY(check_dims(T, D, E, k));
+  if (T == 0) return MOE_OK;
+  if (!x || !gate || !out) return MOE_E_NULLPTR;
+  if (!aligned(x, 4) || !aligned(gate, 4) || (bias && !aligned(bias, 4)) || !aligned(out, 4) ||
+      (topk_ids && !aligned(topk_ids, 4)) || (topk_w && !aligned(topk_w, 4)) ||
+      (expert_offsets && !aligned(expert_offsets, 4)) || (sorted_rows && !aligned(sorted_rows, 4)))
+    return MOE_E_ALIGN;
+  if (moe_workspace_bytes(T, D, F, E, k, W->format, flags) > NOALLOC_SCRATCH_BYTES) {
+    if (trace_enabled())
+      fprintf(stderr, "[moe] moe_layer_noalloc: T=%lld needs more than the %zu-byte scratch\n",
+              (long long)T, NOALLOC_SCRATCH_BYTES);
+    return MOE_E_UNSUPPORTED;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  MOE_TRY(scratch_for_device(s, &ws));
+  return layer_impl(x, gate, bias, W, T, k, flags, out, topk_ids, topk_w, expert_offsets,
+                    sorted_rows, ws, s);
 }
 
 moe_status moe_decode_stack(const float* x, int32_t num_layers, const moe_stack_layer* layers,

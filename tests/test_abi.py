@@ -124,6 +124,27 @@ def test_expert_ffn_validation():
                             None, 0, FAKE, 1 << 40, None) == 1
 
 
+def test_layer_noalloc_validation():
+    """The allocation-free layer rejects bad arguments, and shapes whose workspace
+    exceeds its 8 MiB static array, on the host before any HIP call."""
+    L = M.lib()
+    ex = _experts()
+
+    def call(T=4, k=8, x=FAKE, out=FAKE, e=ex):
+        return L.moe_layer_noalloc(x, FAKE, None, ctypes.byref(e), T, k, 0, out, None, None,
+                                   None, None, None)
+    assert call(T=0) == 0
+    assert call(x=None) == 1
+    assert call(out=None) == 1
+    assert call(k=0) == 2
+    assert call(x=FAKE + 2) == 3
+    assert call(e=_experts(format=9)) == 4
+    assert call(T=64) == 6                      # > 8 MiB of workspace at this geometry
+    assert call(T=1024) == 6
+    assert L.moe_workspace_bytes(32, 2048, 768, 128, 8, 1, M.F_PRENORM) <= 8 << 20
+    assert L.moe_workspace_bytes(64, 2048, 768, 128, 8, 1, 0) > 8 << 20
+
+
 def test_workspace_status_validation():
     L = M.lib()
     assert L.moe_workspace_status(None, 1 << 20, 0, None) == 1
