@@ -10,24 +10,29 @@ layers never reuse expert weights, so the 256 MB Infinity Cache cannot serve
 them.  ``value`` = routed MoE-layer tokens/s = 48 * steps / elapsed.
 
 The same run also measures, under ``workloads``:
-  decode_per_layer  the same 48-layer step as 48 moe_layer calls (one fused
+  toy            16 tokens through the toy layer (d_model 256, 16 Q8_0 experts, top-2)
+  decode_per_layer  the same 48-layer decode step as 48 moe_layer calls (one fused
                  launch per layer)
   decode_batch   32 tokens x 16 chained 4-bit layers (residual + RMSNorm)
-  prefill_down   the down projection + combine operator: 1024 tokens routed
-                 top-8 (8192 rows of 768 fp32 activations), 4-bit W_down,
-                 rotating over 16 layers' routers and weights; both the
-                 two-term (hi+lo fp16) and the single-fp16 activation variants
+  prefill_down   the down projection operator: 1024 tokens routed top-8 (8192 rows
+                 of 768 fp32 activations), 4-bit W_down, rotating over 16 layers'
+                 routings and weights; one call = grouping + expert kernels +
+                 weighted combine (the grouping is timed with the operator, as the
+                 reuse-ordering page timed routing with it); both the two-term
+                 (hi+lo fp16) and the single-fp16 activation variants
   prefill_stack  2048 tokens as two 1024-token microbatches through 48 Q8_0
                  layers (residual + RMSNorm), 96 layer calls per pass
-Each reports its time per call, algorithmic GB/s against the 8 TB/s HBM peak
-and algorithmic MFMA TFLOP/s against the 2.5 PFLOP/s dense fp16 peak (the
-matrix cores see fp16 operands; flops are counted once, without the second
-activation term).  Algorithmic bytes = expert weights of the U experts that
-received rows + router matrix + activations in + outputs out.
+Each reports its time per call, algorithmic GB/s against the 8 TB/s HBM peak and
+algorithmic MFMA TFLOP/s against the 2.5166 PFLOP/s dense fp16 peak (flops
+counted once: 2 x rows x K x N per product; the second activation term of the
+split mode is not counted).  Algorithmic bytes = expert weights of the U experts
+that received rows + router matrix + activations in + outputs out.  Each workload
+also carries its own ``cpu_baseline``: the fp64 oracle timed on the host on a
+bounded sample of the same workload.
 
 Prints ONE JSON line.  ``roofline`` reports the dominant kernel of the headline
-workload (the fused decode layer); ``cpu_baseline`` times the fp64 CPU oracle on
-a bounded sample of the headline workload.
+workload (decode_stack_kernel); ``cpu_baseline`` times the fp64 CPU oracle on a
+bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -51,10 +56,11 @@ GATE_BYTES = D * E * 4 + E * 4           # router matrix + bias
 DECODE_ALGO_BYTES = K * Q8_BLOB + GATE_BYTES + 2 * D * 4   # = 41,173,504
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mixture_experts_routed_lineargate_amd", "csrc")
-DECODE_SRC = os.path.join(CSRC, "decode.hip")
 STACK_SRCS = (os.path.join(CSRC, "decode_stack.hip"), os.path.join(CSRC, "decode_common.hpp"))
+GEMM_SRCS = (os.path.join(CSRC, "grouped_gemm.hip"), os.path.join(CSRC, "mfma_frag.hpp"))
 STACK_LAYERS_PER_LAUNCH = 24
-WORKLOADS = ("decode_per_layer", "decode_batch", "prefill_down", "prefill_stack")
+WORKLOADS = ("toy", "decode_per_layer", "decode_batch", "prefill_down", "prefill_stack")
+CPU_BUDGET = {"toy": 2.0, "decode_batch": 6.0, "prefill_down": 6.0, "prefill_stack": 15.0}
 
 
 def parse():
@@ -64,7 +70,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time budget of the headline's cpu_baseline")
     ap.add_argument("--workloads", default=",".join(WORKLOADS),
                     help="comma list of extra workloads to measure (empty for none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -81,58 +88,90 @@ def source_sha(paths) -> str:
     return h.hexdigest()
 
 
-def counter_traffic(kernel_tag: str, srcs):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source (``source_sha256:`` and
-    ``traffic_bytes_per_launch:`` lines of profiles/<kernel_tag>_traffic.md)."""
-    p = os.path.join(PROFILE_DIR, f"{kernel_tag}_traffic.md")
+def counter_traffic(tag: str, srcs, key: str = "traffic_bytes_per_launch"):
+    """HBM bytes from a committed rocprofv3 counter summary (profiles/<tag>_traffic.md),
+    if it was taken on the current kernel source (its ``source_sha256:`` line)."""
+    p = os.path.join(PROFILE_DIR, f"{tag}_traffic.md")
     if not os.path.exists(p):
         return None
     fields = {}
     with open(p) as f:
         for line in f:
-            if ":" in line and line.split(":", 1)[0].strip() in ("source_sha256",
-                                                                 "traffic_bytes_per_launch"):
+            if ":" in line:
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
     if fields.get("source_sha256") != source_sha(srcs):
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields[key])
     except (KeyError, ValueError):
         return None
 
 
-def cpu_baseline(arena, layers_np, budget_s: float):
-    """fp64 oracle on single-token layer calls (distinct layers) for about `budget_s` seconds.
+# ---------------------------------------------------------------------------
+# Oracle timing on the host
+# ---------------------------------------------------------------------------
 
-    The oracle routes first (untimed) so that only the 8 selected experts are
-    copied to the host; the timed call is the whole oracle layer (routing,
-    dequantising the 8 experts, SwiGLU FFNs, combine).
-    """
-    import moe_synth as S
-    from oracle import moe_oracle as O
+def host_threads() -> dict:
+    """Host cores this process may run on, and the BLAS threads numpy uses."""
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        threads = 1
+        blas = None
+    return {"cores": blas if blas else 1, "host_cores": cores, "blas_threads": blas}
+
+
+def oracle_rate(run_one, budget_s: float, max_n: int, per_call: float, unit: str, sample: str):
+    """Time run_one(i) (the timed part only, as returned) until budget_s is spent."""
     total, n = 0.0, 0
-    while total < budget_s and n < 2000:
+    while total < budget_s and n < max_n:
+        total += run_one(n)
+        n += 1
+    r = {"value": round(n * per_call / total, 4), "unit": unit, "kind": "oracle",
+         "sample": sample.format(n=n, s=total)}
+    r.update(host_threads())
+    return r
+
+
+def host_experts(arena_l, ids, fmt, Dm=D, Fm=F, which=None):
+    import moe_synth as S
+    from oracle import moe_oracle as O
+    host = {}
+    for e in sorted(set(int(e) for e in ids)):
+        g, u, d = S.split_blob(arena_l[e].cpu().numpy(), Dm, Fm, fmt)
+        host[e] = (g, u, d) if which is None else tuple(m if n in which else None
+                                                        for n, m in zip(("gate", "up", "down"),
+                                                                        (g, u, d)))
+    return O.Experts(lambda e: host[e], fmt)
+
+
+def cpu_decode(arena, layers_np, budget_s: float):
+    """Headline: single-token Q8_0 layers on distinct layers of the arena.  The oracle
+    routes first (untimed) so that only the 8 selected experts are copied to the host;
+    the timed call is the whole oracle layer (routing, dequantising the 8 experts,
+    SwiGLU FFNs, combine)."""
+    import moe_synth as S
+    from oracle import moe_oracle as O
+
+    def one(n):
         l = (7 * n + 3) % len(layers_np)
         G, b = layers_np[l]
         x = S.hidden(2, 1, D, layer=1000 + n)
         ids = O.select_topk(O.router_logits(x, G, b), K)[0]
-        host = {int(e): S.split_blob(arena[l, int(e)].cpu().numpy(), D, F, S.FMT_Q8_0) for e in ids}
-        ex = O.Experts(lambda e, host=host: host[e], S.FMT_Q8_0)
+        ex = host_experts(arena[l], ids, S.FMT_Q8_0)
         t0 = time.perf_counter()
         O.moe_layer(x, G, b, ex, K, residual=True)
-        total += time.perf_counter() - t0
-        n += 1
-    return {"value": round(n / total, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} single-token Q8_0 decode layer calls on distinct layers (fp64 numpy oracle: "
-                      f"routing, dequantising the 8 selected experts, SwiGLU, combine); {total:.1f} s"}
+        return time.perf_counter() - t0
+    return oracle_rate(one, budget_s, 2000, 1.0, "tokens/s",
+                       "{n} single-token Q8_0 decode layer calls on distinct layers (fp64 numpy "
+                       "oracle: routing, dequantising the 8 selected experts, SwiGLU, combine); {s:.1f} s")
 
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
 
 def graph_time_ms(torch, fn, stream, warmup: int, iters: int) -> float:
     """Capture fn() once as a HIP graph; return the mean ms per replay (events on `stream`)."""
@@ -159,38 +198,63 @@ def n_active(torch, ids) -> int:
     return int(torch.unique(ids).numel())
 
 
-def rates(ms: float, nbytes: float, flops: float, ffn: float = 0.0, split: bool = True) -> dict:
-    """Algorithmic rates; `ffn` = the expert-FFN share of `flops`.  With split fp16
-    activations every algorithmic product costs two fp16 MFMA products, so the
-    dequant-adjusted peak for the expert FFN is half the fp16 peak (fp16-only
-    activations: the full peak)."""
+def rates(ms: float, nbytes: float, flops: float) -> dict:
+    """Algorithmic rates against the HBM and dense fp16 MFMA peaks."""
     s = ms / 1e3
     gbps = nbytes / s / 1e9
     tf = flops / s / 1e12
-    r = {"ms_per_call": round(ms, 5), "algorithmic_bytes": int(nbytes),
-         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-         "mfma_tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_FP16_PEAK_TFLOPS, 4)}
-    if ffn > 0:
-        adj = MFMA_FP16_PEAK_TFLOPS / (2.0 if split else 1.0)
-        r["ffn_mfma_adjusted_peak_tflops"] = round(adj, 1)
-        r["ffn_mfma_adjusted_frac"] = round(ffn / s / 1e12 / adj, 4)
+    return {"ms_per_call": round(ms, 5), "algorithmic_bytes": int(nbytes),
+            "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "mfma_tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_FP16_PEAK_TFLOPS, 4)}
+
+
+def ffn_flops(rows: int, Dm: int = D, Fm: int = F) -> float:
+    return 2.0 * rows * Dm * Fm * 3
+
+
+def bench_toy(torch, M, S, dev, stream, iters, cpu):
+    """16 tokens through the toy layer (d_model 256, d_ff 128, 16 Q8_0 experts, top-2)."""
+    from oracle import moe_oracle as O
+    T, Dm, Fm, Em, k = 16, 256, 128, 16, 2
+    G = S.gate_matrix(1, Dm, Em)
+    x = S.hidden(1, T, Dm)
+    blobs = S.expert_blobs(1, Em, Dm, Fm, S.FMT_Q8_0)
+    ex = M.Experts.from_blobs(torch.from_numpy(blobs).to(dev), Dm, Fm, S.FMT_Q8_0)
+    tx, tG = torch.from_numpy(x).to(dev), torch.from_numpy(G).to(dev)
+    out = torch.empty((T, Dm), dtype=torch.float32, device=dev)
+    ws = M.workspace(T, Dm, Fm, Em, k, S.FMT_Q8_0)
+
+    def one():
+        M.moe_layer(tx, tG, None, ex, k, out, ws=ws, stream=stream)
+    ms = graph_time_ms(torch, one, stream, 3, max(iters, 20))
+    r = {"workload": "toy layer: 16 tokens x d_model 256, 16 Q8_0 experts (256x128 / 128x256), "
+                     "top-2, no bias (latency-bound; correctness config)",
+         "tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_call": round(ms, 5)}
+    if cpu:
+        oex = O.Experts(lambda e: S.split_blob(blobs[e], Dm, Fm, S.FMT_Q8_0), S.FMT_Q8_0)
+
+        def run(n):
+            t0 = time.perf_counter()
+            O.moe_layer(x, G, None, O.Experts(oex.fetch, S.FMT_Q8_0), k)
+            return time.perf_counter() - t0
+        r["cpu_baseline"] = oracle_rate(run, CPU_BUDGET["toy"], 500, T, "tokens/s",
+                                        "{n} calls of the whole 16-token toy layer (fp64 oracle, "
+                                        "experts decoded per call); {s:.1f} s")
     return r
 
 
-def ffn_flops(rows: int) -> float:
-    return 2.0 * rows * D * F * 3
-
-
-def bench_decode_batch(torch, M, S, dev, stream, iters):
+def bench_decode_batch(torch, M, S, dev, stream, iters, cpu):
     """32 tokens through 16 chained 4-bit layers (residual + RMSNorm), one graph per pass."""
+    from oracle import moe_oracle as O
     T, L4 = 32, 16
     arena = S.device_arena(3, L4, E, D, F, S.FMT_Q4, dev)
-    gates = [(torch.from_numpy(S.gate_matrix(3, D, E, layer=l)).to(dev),
-              torch.from_numpy(S.zipf_bias(3, E, layer=l)).to(dev)) for l in range(L4)]
+    gnp = [(S.gate_matrix(3, D, E, layer=l), S.zipf_bias(3, E, layer=l)) for l in range(L4)]
+    gates = [(torch.from_numpy(G).to(dev), torch.from_numpy(b).to(dev)) for G, b in gnp]
     ex = [M.Experts.from_blobs(arena[l], D, F, S.FMT_Q4) for l in range(L4)]
     flags = M.F_RESIDUAL | M.F_PRENORM
     ws = M.workspace(T, D, F, E, K, S.FMT_Q4, flags)
-    bufs = [torch.from_numpy(S.hidden(3, T, D)).to(dev)] + \
+    x0 = S.hidden(3, T, D)
+    bufs = [torch.from_numpy(x0).to(dev)] + \
            [torch.empty((T, D), dtype=torch.float32, device=dev) for _ in range(L4)]
     ids = torch.empty((L4, T, K), dtype=torch.int32, device=dev)
 
@@ -200,19 +264,38 @@ def bench_decode_batch(torch, M, S, dev, stream, iters):
                         flags=flags if l > 0 else M.F_RESIDUAL, topk_ids=ids[l], ws=ws,
                         stream=stream)
     ms = graph_time_ms(torch, one, stream, 3, iters) / L4
+    M.check_workspace(ws, stream=stream)
     U = sum(n_active(torch, ids[l]) for l in range(L4)) / L4
     nbytes = U * Q4_BLOB + GATE_BYTES + 2 * T * D * 4
     flops = ffn_flops(T * K) + 2.0 * T * D * E
     r = {"workload": "decode batch: 32 tokens x Qwen3-MoE layer, 4-bit experts, Zipf router, top-8; "
                      "16 distinct layers chained (residual + RMSNorm)",
          "tokens_per_s": round(T / (ms / 1e3), 1), "mean_active_experts": round(U, 2)}
-    r.update(rates(ms, nbytes, flops, ffn=ffn_flops(T * K)))
+    r.update(rates(ms, nbytes, flops))
+    traffic = counter_traffic("decode_batch_q4_layer", (os.path.join(CSRC, "skinny_gemm.hip"),
+                                                        os.path.join(CSRC, "route_small.hip")))
+    r["traffic"] = traffic
+    if cpu:
+        def run(n):
+            l = n % L4
+            G, b = gnp[l]
+            xl = S.hidden(3, T, D, layer=2000 + n)
+            eids = O.select_topk(O.router_logits(xl, G, b), K)
+            oex = host_experts(arena[l], eids.ravel(), S.FMT_Q4)
+            t0 = time.perf_counter()
+            O.moe_layer(xl, G, b, oex, K, residual=True)
+            return time.perf_counter() - t0
+        r["cpu_baseline"] = oracle_rate(run, CPU_BUDGET["decode_batch"], 200, T, "tokens/s",
+                                        "{n} calls of one whole 32-token 4-bit layer (fp64 oracle: "
+                                        "routing, dequantising the active experts, SwiGLU, "
+                                        "combine); {s:.1f} s")
     del arena
-    return r, ws
+    return r
 
 
-def bench_prefill_down(torch, M, S, dev, stream, iters):
-    """Down projection + combine over 8192 routed rows, rotating over 16 layers."""
+def bench_prefill_down(torch, M, S, dev, stream, iters, cpu):
+    """Grouping + down projection + combine over 8192 routed rows, rotating over 16 layers."""
+    from oracle import moe_oracle as O
     T, L4 = 1024, 16
     R = T * K
     arena = S.device_arena(4, L4, E, D, F, S.FMT_Q4, dev, which=("down",))
@@ -226,43 +309,61 @@ def bench_prefill_down(torch, M, S, dev, stream, iters):
     w = torch.empty((L4, T, K), dtype=torch.float32, device=dev)
     offs = torch.empty((L4, E + 1), dtype=torch.int32, device=dev)
     rows = torch.empty((L4, R), dtype=torch.int32, device=dev)
-    for l in range(L4):       # routing by this library's router (setup, untimed)
+    for l in range(L4):       # the operator's input routing (setup, untimed)
         G = torch.from_numpy(S.gate_matrix(4, D, E, layer=l)).to(dev)
         b = torch.from_numpy(S.zipf_bias(4, E, layer=l)).to(dev)
         M.moe_route(xr, G, b, K, ids[l], w[l], ws)
-        M.moe_group(ids[l], E, offs[l], rows[l], ws)
     torch.cuda.synchronize()
     out = torch.empty((T, D), dtype=torch.float32, device=dev)
     U = sum(n_active(torch, ids[l]) for l in range(L4)) / L4
     nbytes = U * Q4_DOWN + R * F * 4 + T * D * 4 + R * 4 * 3 + (E + 1) * 4
     flops = 2.0 * R * F * D
-    res = {"workload": "prefill down projection + combine: 1024 tokens routed top-8 of 128 "
-                       "(8192 rows x 768 fp32), 4-bit W_down 768x2048, Zipf routers; "
-                       "rotating over 16 layers",
+    res = {"workload": "prefill down projection operator: 1024 tokens routed top-8 of 128 "
+                       "(8192 rows x 768 fp32), 4-bit W_down 768x2048, Zipf routers; one call = "
+                       "grouping + expert kernels + weighted combine; rotating over 16 layers",
            "mean_active_experts": round(U, 2)}
     # split_fp16_banded: the same operator with the output tiles walked in bands of
     # four (the reuse-ordering page's traversal; bit-identical results)
     for name, fl in (("split_fp16", 0), ("fp16", M.F_FP16_ACT), ("split_fp16_banded", M.F_BANDED)):
         def one(fl=fl):
             for l in range(L4):
+                M.moe_group(ids[l], E, offs[l], rows[l], ws, stream=stream)
                 M.moe_expert_ffn(h, M.STAGE_DOWN, ex[l], ids[l], w[l], offs[l], rows[l],
                                  out=out, flags=fl, ws=ws, stream=stream)
         ms = graph_time_ms(torch, one, stream, 3, iters) / L4
         r = {"tokens_per_s": round(T / (ms / 1e3), 1)}
-        r.update(rates(ms, nbytes, flops, ffn=flops, split=not (fl & M.F_FP16_ACT)))
+        r.update(rates(ms, nbytes, flops))
         res[name] = r
+    res["traffic"] = counter_traffic("prefill_down_q4_operator", GEMM_SRCS)
+    if cpu:
+        hs = h[:256 * K].cpu().numpy()
+
+        def run(n):
+            l = n % L4
+            tid = ids[l, :256].cpu().numpy()
+            tw = w[l, :256].cpu().numpy()
+            oex = host_experts(arena[l], tid.ravel(), S.FMT_Q4, which=("down",))
+            t0 = time.perf_counter()
+            O.down_combine(hs, tid, tw, oex)
+            return time.perf_counter() - t0
+        res["cpu_baseline"] = oracle_rate(run, CPU_BUDGET["prefill_down"], 100, 256, "tokens/s",
+                                          "{n} calls of the operator on 256 of the 1024 tokens "
+                                          "(2048 routed rows; fp64 oracle: dequantising the "
+                                          "active W_down, products, combine); {s:.1f} s")
     del arena
     return res
 
 
-def bench_prefill_stack(torch, M, S, dev, stream, arena, gates, iters):
+def bench_prefill_stack(torch, M, S, dev, stream, arena, layers_np, gates, iters, cpu):
     """2048 tokens as 2 x 1024 through 48 Q8_0 layers (residual + RMSNorm)."""
+    from oracle import moe_oracle as O
     T, MB = 2048, 1024
     L = arena.shape[0]
     ex = [M.Experts.from_blobs(arena[l], D, F, S.FMT_Q8_0) for l in range(L)]
     flags = M.F_RESIDUAL | M.F_PRENORM
     ws = M.workspace(MB, D, F, E, K, S.FMT_Q8_0, flags)
-    x0 = torch.from_numpy(S.hidden(5, T, D)).to(dev)
+    x0np = S.hidden(5, T, D)
+    x0 = torch.from_numpy(x0np).to(dev)
     outs = torch.empty((L, T, D), dtype=torch.float32, device=dev)
     ids = torch.empty((L, T, K), dtype=torch.int32, device=dev)
 
@@ -275,6 +376,7 @@ def bench_prefill_stack(torch, M, S, dev, stream, arena, gates, iters):
                             flags=flags if l > 0 else M.F_RESIDUAL, topk_ids=ids[l, sl], ws=ws,
                             stream=stream)
     ms = graph_time_ms(torch, one, stream, 2, iters)
+    M.check_workspace(ws, stream=stream)
     if not torch.isfinite(outs[L - 1]).all():
         raise RuntimeError("prefill stack: non-finite output")
     Us = [n_active(torch, ids[l, mb * MB:(mb + 1) * MB]) for mb in range(T // MB) for l in range(L)]
@@ -285,11 +387,37 @@ def bench_prefill_stack(torch, M, S, dev, stream, arena, gates, iters):
          "tokens_per_s": round(T / (ms / 1e3), 1),
          "token_layers_per_s": round(T * L / (ms / 1e3), 1),
          "mean_active_experts": round(sum(Us) / len(Us), 2)}
-    r.update(rates(ms, nbytes, flops, ffn=len(Us) * ffn_flops(MB * K)))
+    r.update(rates(ms, nbytes, flops))
     r["ms_per_call"] = round(ms / len(Us), 5)
     r["ms_per_pass"] = round(ms, 4)
+    r["traffic_per_microbatch_layer"] = counter_traffic("prefill_layer_q8_0", GEMM_SRCS)
+    if cpu:
+        # once: a 2-token sample (one from each microbatch) through all 48 layers
+        sample = x0np[[5, MB + 5]]
+
+        def layers():
+            for l in range(L):
+                yield layers_np[l][0], layers_np[l][1], lazy_layer(arena[l])
+
+        t0 = time.perf_counter()
+        O.stack(sample, layers(), K)
+        dt = time.perf_counter() - t0
+        r["cpu_baseline"] = {"value": round(2 * L / dt, 4), "unit": "token-layers/s",
+                             "kind": "oracle",
+                             "sample": f"2 tokens (one per microbatch) through all 48 layers, once "
+                                       f"(fp64 oracle stack: routing, dequantising each selected "
+                                       f"expert, SwiGLU, combine, residual, RMSNorm); {dt:.1f} s"}
+        r["cpu_baseline"].update(host_threads())
     del outs
     return r
+
+
+def lazy_layer(arena_l):
+    """The oracle's Experts over one Q8_0 layer of a device arena, bytes fetched per expert."""
+    import moe_synth as S
+    from oracle import moe_oracle as O
+    return O.Experts(lambda e: S.split_blob(arena_l[e].cpu().numpy(), D, F, S.FMT_Q8_0),
+                     S.FMT_Q8_0)
 
 
 def main():
@@ -305,6 +433,7 @@ def main():
 
     dev = torch.device("cuda:0")
     L = a.layers
+    cpu = not a.no_cpu_baseline
     arena = S.device_arena(2, L, E, D, F, S.FMT_Q8_0, dev)          # [L][E][stride]
     layers_np = [(S.gate_matrix(2, D, E, layer=l), S.zipf_bias(2, E, layer=l)) for l in range(L)]
     gates = [(torch.from_numpy(G).to(dev), torch.from_numpy(b).to(dev)) for G, b in layers_np]
@@ -373,6 +502,11 @@ def main():
         },
     }
     extra = {}
+    iters = max(3, min(20, a.steps // 10))
+    if "toy" in want:
+        extra["toy"] = bench_toy(torch, M, S, dev, stream, iters, cpu)
+        print(f"[bench] toy: {extra['toy']['ms_per_call'] * 1e3:.2f} us per call", file=sys.stderr,
+              flush=True)
     if "decode_per_layer" in want:
         bufs = [x0] + [torch.empty((1, D), dtype=torch.float32, device=dev) for _ in range(L)]
 
@@ -389,30 +523,31 @@ def main():
             "tokens_per_s": round(L / (ms_pl / 1e3), 1),
             "us_per_layer": round(ms_pl * 1e3 / L, 3),
             "hbm_gbps": round(DECODE_ALGO_BYTES / (ms_pl / 1e3 / L) / 1e9, 1),
+            "hbm_frac": round(DECODE_ALGO_BYTES / (ms_pl / 1e3 / L) / 1e9 / HBM_PEAK_GBPS, 4),
             "max_rel_diff_vs_stack": diff,
         }
         print(f"[bench] decode per layer: {ms_pl * 1e3 / L:.2f} us per layer call",
               file=sys.stderr, flush=True)
-    iters = max(3, min(20, a.steps // 10))
     if "decode_batch" in want:
-        extra["decode_batch"], _ = bench_decode_batch(torch, M, S, dev, stream, iters)
+        extra["decode_batch"] = bench_decode_batch(torch, M, S, dev, stream, iters, cpu)
         print(f"[bench] decode_batch: {extra['decode_batch']['ms_per_call'] * 1e3:.2f} us per layer",
               file=sys.stderr, flush=True)
     if "prefill_down" in want:
-        extra["prefill_down"] = bench_prefill_down(torch, M, S, dev, stream, iters)
-        print(f"[bench] prefill_down: {extra['prefill_down']['split_fp16']['ms_per_call'] * 1e3:.2f} "
-              f"/ {extra['prefill_down']['fp16']['ms_per_call'] * 1e3:.2f} "
-              f"/ banded {extra['prefill_down']['split_fp16_banded']['ms_per_call'] * 1e3:.2f} us per call",
+        extra["prefill_down"] = bench_prefill_down(torch, M, S, dev, stream, iters, cpu)
+        pdn = extra["prefill_down"]
+        print(f"[bench] prefill_down: {pdn['split_fp16']['ms_per_call'] * 1e3:.2f} "
+              f"/ {pdn['fp16']['ms_per_call'] * 1e3:.2f} "
+              f"/ banded {pdn['split_fp16_banded']['ms_per_call'] * 1e3:.2f} us per call",
               file=sys.stderr, flush=True)
     if "prefill_stack" in want:
-        extra["prefill_stack"] = bench_prefill_stack(torch, M, S, dev, stream, arena, gates,
-                                                     max(2, iters // 4))
+        extra["prefill_stack"] = bench_prefill_stack(torch, M, S, dev, stream, arena, layers_np,
+                                                     gates, max(2, iters // 4), cpu)
         print(f"[bench] prefill_stack: {extra['prefill_stack']['ms_per_pass']:.3f} ms per pass",
               file=sys.stderr, flush=True)
     if extra:
         line["workloads"] = extra
-    if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(arena, layers_np, a.cpu_seconds)
+    if cpu:
+        line["cpu_baseline"] = cpu_decode(arena, layers_np, a.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
