@@ -57,7 +57,11 @@ DECODE_ALGO_BYTES = K * Q8_BLOB + GATE_BYTES + 2 * D * 4   # = 41,173,504
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mixture_experts_routed_lineargate_amd", "csrc")
 STACK_SRCS = (os.path.join(CSRC, "decode_stack.hip"), os.path.join(CSRC, "decode_common.hpp"))
-GEMM_SRCS = (os.path.join(CSRC, "grouped_gemm.hip"), os.path.join(CSRC, "mfma_frag.hpp"))
+DOWN_OP_SRCS = tuple(os.path.join(CSRC, f) for f in ("grouped_gemm.hip", "mfma_frag.hpp",
+                                                     "ffn_generic.hip", "group.hip"))
+PREFILL_SRCS = DOWN_OP_SRCS + (os.path.join(CSRC, "router.hip"),)
+BATCH_SRCS = tuple(os.path.join(CSRC, f) for f in ("skinny_gemm.hip", "route_small.hip",
+                                                   "mfma_frag.hpp", "ffn_generic.hip"))
 STACK_LAYERS_PER_LAUNCH = 24
 WORKLOADS = ("toy", "decode_per_layer", "decode_batch", "prefill_down", "prefill_stack")
 CPU_BUDGET = {"toy": 2.0, "decode_batch": 6.0, "prefill_down": 6.0, "prefill_stack": 15.0}
@@ -272,9 +276,7 @@ def bench_decode_batch(torch, M, S, dev, stream, iters, cpu):
                      "16 distinct layers chained (residual + RMSNorm)",
          "tokens_per_s": round(T / (ms / 1e3), 1), "mean_active_experts": round(U, 2)}
     r.update(rates(ms, nbytes, flops))
-    traffic = counter_traffic("decode_batch_q4_layer", (os.path.join(CSRC, "skinny_gemm.hip"),
-                                                        os.path.join(CSRC, "route_small.hip")))
-    r["traffic"] = traffic
+    r["traffic"] = counter_traffic("decode_batch_q4_layer", BATCH_SRCS)
     if cpu:
         def run(n):
             l = n % L4
@@ -334,7 +336,7 @@ def bench_prefill_down(torch, M, S, dev, stream, iters, cpu):
         r = {"tokens_per_s": round(T / (ms / 1e3), 1)}
         r.update(rates(ms, nbytes, flops))
         res[name] = r
-    res["traffic"] = counter_traffic("prefill_down_q4_operator", GEMM_SRCS)
+    res["traffic"] = counter_traffic("prefill_down_q4_operator", DOWN_OP_SRCS)
     if cpu:
         hs = h[:256 * K].cpu().numpy()
 
@@ -390,7 +392,7 @@ def bench_prefill_stack(torch, M, S, dev, stream, arena, layers_np, gates, iters
     r.update(rates(ms, nbytes, flops))
     r["ms_per_call"] = round(ms / len(Us), 5)
     r["ms_per_pass"] = round(ms, 4)
-    r["traffic_per_microbatch_layer"] = counter_traffic("prefill_layer_q8_0", GEMM_SRCS)
+    r["traffic_per_microbatch_layer"] = counter_traffic("prefill_layer_q8_0", PREFILL_SRCS)
     if cpu:
         # once: a 2-token sample (one from each microbatch) through all 48 layers
         sample = x0np[[5, MB + 5]]
