@@ -22,6 +22,8 @@ layer, learned top-8 selection by a LinearGate router):
            (SwiGLU as defined by Shazeer, "GLU Variants Improve Transformer")
 6. combine out_t = sum_j w_{t,j} y_{t,j}  (+ x_t with a residual)
 7. stack   o_l = in_l + MoE_l(in_l), in_{l+1} = o_l / sqrt(mean(o_l^2) + eps)
+8. attention-side primitives of the warm path: input RMSNorm with gain, Q/K/V
+   projection, per-head Q/K RMSNorm, RoPE, KV append
 
 Block formats (weights are "native Q8_0", evidence page, GPU-native foundation
 card; "Q4 expert execution", technical-overview page, Execution architecture):
@@ -285,3 +287,59 @@ def stack(x0, layers, k: int, eps: float = 1e-6, on_layer=None) -> list:
             on_layer(l, r)
         res.append(r)
     return res
+
+
+# ---------------------------------------------------------------------------
+# 8. Attention-side primitives of the warm decode path (technical-overview page,
+#    "Validated GPU foundation": RMSNorm, grouped per-head Q/K normalization,
+#    Q/K/V projections, RoPE, request-local F32 KV append).  Attention itself
+#    (scores, softmax, value aggregation, output projection) is not here: the
+#    same page lists it as still being integrated.
+# ---------------------------------------------------------------------------
+
+def rmsnorm_gain(x, gain, eps: float = 1e-6) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * gain over the last axis."""
+    return rmsnorm(x, eps) * np.asarray(gain, dtype=np.float64)
+
+
+def rope(x, pos, theta: float) -> np.ndarray:
+    """Rotary position embedding, rotate-half pairing: for i < hd/2 the pair
+    (x_i, x_{i+hd/2}) is rotated by the angle pos * theta^(-2i/hd).
+
+    ``x`` [T][H][hd], ``pos`` [T] (integers)."""
+    x = np.asarray(x, dtype=np.float64)
+    hd = x.shape[-1]
+    half = hd // 2
+    inv_freq = theta ** (-np.arange(half, dtype=np.float64) * 2.0 / hd)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]      # [T][half]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def attn_prep(x, w_qkv_raw, fmt: int, attn_gain, q_gain, k_gain, pos, theta: float,
+              n_q: int, n_kv: int, head_dim: int, eps: float = 1e-6) -> dict:
+    """One token block through the attention-side primitives:
+    u = rmsnorm(x) * attn_gain; [q | k | v] = u W_qkv (rows of blocks: n_q heads
+    of q, then n_kv of k, then n_kv of v, head_dim rows each); per-head
+    RMSNorm of q and k with the shared gains q_gain / k_gain [head_dim]; RoPE
+    of q and k at each token's position.  Returns q [T][n_q][hd], and the k and
+    v rows [T][n_kv][hd] that the KV append writes at row pos[t] of the cache."""
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    u = rmsnorm_gain(x, attn_gain, eps)
+    qkv = u @ dequant_matrix(w_qkv_raw, fmt)
+    nq, nk = n_q * head_dim, n_kv * head_dim
+    q = qkv[:, :nq].reshape(T, n_q, head_dim)
+    k = qkv[:, nq:nq + nk].reshape(T, n_kv, head_dim)
+    v = qkv[:, nq + nk:nq + 2 * nk].reshape(T, n_kv, head_dim)
+    q = rope(rmsnorm_gain(q, q_gain, eps), pos, theta)
+    k = rope(rmsnorm_gain(k, k_gain, eps), pos, theta)
+    return {"u": u, "qkv": qkv, "q": q, "k": k, "v": v}
+
+
+def kv_append(k_cache, v_cache, k, v, pos) -> None:
+    """Write token t's k and v rows at row pos[t] of the caches ([max_pos][n_kv][hd])."""
+    for t, p in enumerate(np.asarray(pos)):
+        k_cache[int(p)] = k[t]
+        v_cache[int(p)] = v[t]

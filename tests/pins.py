@@ -481,13 +481,102 @@ def pin_topk_gap(O):
     assert O.topk_gap(np.array([[3.0, 1.0, 0.25, 0.0]]), 2)[0] == 0.75
 
 
+# ---------------------------------------------------------------------------
+# Attention-side primitives (input norm, Q/K/V projection, per-head Q/K norm,
+# RoPE, KV append)
+# ---------------------------------------------------------------------------
+
+def _rope_complex(x, pos, theta):
+    """RoPE as complex multiplication: z_i = x_i + j x_{i+hd/2} times e^{j pos theta^(-2i/hd)}."""
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
+    z = x[..., :half] + 1j * x[..., half:]
+    freq = theta ** (-2.0 * np.arange(half) / x.shape[-1])
+    rot = np.exp(1j * np.asarray(pos, dtype=np.float64)[:, None, None] * freq[None, None, :])
+    w = z * rot
+    return np.concatenate([w.real, w.imag], axis=-1)
+
+
+def pin_rope(O):
+    """RoPE equals rotation of the complex pairs (x_i, x_{i+hd/2}); it preserves each
+    pair's norm, is the identity at position 0, and q.k after RoPE depends only on the
+    position difference."""
+    rng = np.random.default_rng(19)
+    x = rng.standard_normal((6, 3, 64))
+    pos = np.array([0, 1, 7, 100, 4095, 8191])
+    got = O.rope(x, pos, 1e6)
+    assert np.allclose(got, _rope_complex(x, pos, 1e6), rtol=0, atol=1e-12)
+    assert np.array_equal(got[0], x[0])
+    half = 32
+    pn = lambda a: a[..., :half] ** 2 + a[..., half:] ** 2      # noqa: E731
+    assert np.allclose(pn(got), pn(x), rtol=1e-12, atol=1e-12)
+    q, k = rng.standard_normal((1, 1, 64)), rng.standard_normal((1, 1, 64))
+    for m, n in ((5, 2), (900, 17), (3, 3)):
+        a = (O.rope(q, [m], 1e4) * O.rope(k, [n], 1e4)).sum()
+        b = (O.rope(q, [m - n], 1e4) * O.rope(k, [0], 1e4)).sum()
+        assert abs(a - b) < 1e-9 * (1 + abs(a)), (m, n, a, b)
+
+
+def pin_rmsnorm_gain(O):
+    import torch
+    rng = np.random.default_rng(20)
+    x = rng.standard_normal((5, 4, 128)) * 2
+    g = 1 + 0.1 * rng.standard_normal(128)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (128,), weight=torch.from_numpy(g),
+                                       eps=1e-6).numpy()
+    assert np.allclose(O.rmsnorm_gain(x, g, 1e-6), ref, rtol=1e-13, atol=0)
+
+
+def pin_attn_prep(O):
+    """The whole primitive chain against a torch float64 composition written out here:
+    rms_norm(x, gain) -> u W (exact block matrix; rows ordered q heads, k heads, v heads)
+    -> per-head rms_norm with the q / k gains -> RoPE by complex multiplication; v is
+    neither normalised nor rotated."""
+    import torch
+    import torch.nn.functional as Fn
+    rng = np.random.default_rng(21)
+    D, nq, nkv, hd = 96, 3, 2, 32
+    for fmt in (O.Q8_0, O.Q4):
+        W, raw = _exact_matrix(rng, D, (nq + 2 * nkv) * hd, fmt)
+        x = rng.standard_normal((4, D)).astype(np.float32) * 3
+        ga = (1 + 0.2 * rng.standard_normal(D)).astype(np.float32)
+        gq = (1 + 0.2 * rng.standard_normal(hd)).astype(np.float32)
+        gk = (1 + 0.2 * rng.standard_normal(hd)).astype(np.float32)
+        pos = np.array([0, 3, 17, 250])
+        r = O.attn_prep(x, raw, fmt, ga, gq, gk, pos, 1e6, nq, nkv, hd)
+        t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))       # noqa: E731
+        u = Fn.rms_norm(t(x), (D,), weight=t(ga), eps=1e-6)
+        qkv = (u @ t(W)).numpy()
+        q = qkv[:, :nq * hd].reshape(4, nq, hd)
+        k = qkv[:, nq * hd:(nq + nkv) * hd].reshape(4, nkv, hd)
+        v = qkv[:, (nq + nkv) * hd:].reshape(4, nkv, hd)
+        q = _rope_complex(Fn.rms_norm(t(q), (hd,), weight=t(gq), eps=1e-6).numpy(), pos, 1e6)
+        k = _rope_complex(Fn.rms_norm(t(k), (hd,), weight=t(gk), eps=1e-6).numpy(), pos, 1e6)
+        for name, ref in (("q", q), ("k", k), ("v", v)):
+            assert np.allclose(r[name], ref, rtol=1e-11, atol=1e-11), (fmt, name)
+
+
+def pin_kv_append(O):
+    """Token t's k and v land at row pos[t] of the caches; no other row changes."""
+    rng = np.random.default_rng(22)
+    kc, vc = np.full((10, 2, 4), 7.0), np.full((10, 2, 4), -7.0)
+    k, v = rng.standard_normal((3, 2, 4)), rng.standard_normal((3, 2, 4))
+    pos = np.array([4, 0, 9])
+    O.kv_append(kc, vc, k, v, pos)
+    for t, p_ in enumerate(pos):
+        assert np.array_equal(kc[p_], k[t]) and np.array_equal(vc[p_], v[t])
+    rest = np.setdiff1d(np.arange(10), pos)
+    assert (kc[rest] == 7.0).all() and (vc[rest] == -7.0).all()
+
+
 ALL_PINS = [
     pin_page_expert_size, pin_fp16_decoder, pin_q8_0_exhaustive, pin_q4_exhaustive,
     pin_matrix_orientation, pin_encoder_roundtrip, pin_topk_bruteforce, pin_tie_break_zero_gate,
     pin_weights_closed_form, pin_full_selection_is_softmax, pin_router_logits, pin_grouping,
     pin_dense_reduction, pin_all_experts_mixture, pin_zero_input, pin_scalar_bruteforce,
     pin_linearity, pin_equivariance, pin_down_combine, pin_rmsnorm, pin_stack_zero_experts,
-    pin_stack_live_experts, pin_topk_gap,
+    pin_stack_live_experts, pin_topk_gap, pin_rope, pin_rmsnorm_gain, pin_attn_prep,
+    pin_kv_append,
 ]
 
 

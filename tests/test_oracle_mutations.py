@@ -168,6 +168,57 @@ def _gap_off_by_one(logits, k):
     return s[:, k] - s[:, k + 1]
 
 
+def _rope_negative_angle(x, pos, theta):
+    return _orig["rope"](x, -np.asarray(pos), theta)
+
+
+def _rope_interleaved(x, pos, theta):
+    x = np.asarray(x, dtype=np.float64)
+    hd = x.shape[-1]
+    perm = np.concatenate([np.arange(0, hd, 2), np.arange(1, hd, 2)])
+    inv = np.argsort(perm)
+    return _orig["rope"](x[..., perm], pos, theta)[..., inv]
+
+
+def _rope_half_frequency(x, pos, theta):
+    return _orig["rope"](x, pos, theta ** 0.5)
+
+
+def _attn_norm_over_all_heads(x, w_qkv_raw, fmt, attn_gain, q_gain, k_gain, pos, theta, n_q,
+                              n_kv, head_dim, eps=1e-6):
+    r = _orig["attn_prep"](x, w_qkv_raw, fmt, attn_gain, q_gain, k_gain, pos, theta, n_q, n_kv,
+                           head_dim, eps)
+    T = r["qkv"].shape[0]
+    q = r["qkv"][:, :n_q * head_dim]
+    q = O.rmsnorm(q, eps).reshape(T, n_q, head_dim) * np.asarray(q_gain, np.float64)
+    r["q"] = O.rope(q, pos, theta)
+    return r
+
+
+def _attn_v_normalised(*a, **kw):
+    r = _orig["attn_prep"](*a, **kw)
+    r["v"] = O.rmsnorm(r["v"])
+    return r
+
+
+def _attn_k_not_rotated(x, w_qkv_raw, fmt, attn_gain, q_gain, k_gain, pos, theta, n_q, n_kv,
+                        head_dim, eps=1e-6):
+    r = _orig["attn_prep"](x, w_qkv_raw, fmt, attn_gain, q_gain, k_gain, pos, theta, n_q, n_kv,
+                           head_dim, eps)
+    T = r["qkv"].shape[0]
+    k = r["qkv"][:, n_q * head_dim:(n_q + n_kv) * head_dim].reshape(T, n_kv, head_dim)
+    r["k"] = O.rmsnorm_gain(k, k_gain, eps)
+    return r
+
+
+def _rmsnorm_gain_dropped(x, gain, eps=1e-6):
+    return O.rmsnorm(x, eps)
+
+
+def _kv_append_off_by_one(k_cache, v_cache, k, v, pos):
+    _orig["kv_append"](k_cache, v_cache, k, v, (np.asarray(pos) + 1) % k_cache.shape[0])
+
+
 MUTATIONS = {
     "q4 nibble order swapped": ("decode_rows", _decode_nibbles_swapped),
     "q4 missing -8": ("decode_rows", _decode_no_offset),
@@ -190,6 +241,14 @@ MUTATIONS = {
     "stack normalises in_l instead of o_l": ("stack", _stack_normalises_input),
     "gap rule vacuous": ("topk_gap", _gap_vacuous),
     "gap taken one rank too low": ("topk_gap", _gap_off_by_one),
+    "rope rotates the wrong way": ("rope", _rope_negative_angle),
+    "rope pairs adjacent elements": ("rope", _rope_interleaved),
+    "rope frequencies off": ("rope", _rope_half_frequency),
+    "q normalised over all heads at once": ("attn_prep", _attn_norm_over_all_heads),
+    "v normalised": ("attn_prep", _attn_v_normalised),
+    "k not rotated": ("attn_prep", _attn_k_not_rotated),
+    "norm gain dropped": ("rmsnorm_gain", _rmsnorm_gain_dropped),
+    "kv append one row off": ("kv_append", _kv_append_off_by_one),
 }
 
 
