@@ -22,6 +22,9 @@ The same run also measures, under ``workloads``:
                  (hi+lo fp16) and the single-fp16 activation variants
   prefill_stack  2048 tokens as two 1024-token microbatches through 48 Q8_0
                  layers (residual + RMSNorm), 96 layer calls per pass
+  attn_prep      one decode token through the attention-side primitives (input
+                 RMSNorm, Q8_0 Q/K/V projection 2048 -> 32+4+4 heads of 128,
+                 per-head Q/K RMSNorm, RoPE, KV append), rotating over 48 layers
 Each reports its time per call, algorithmic GB/s against the 8 TB/s HBM peak and
 algorithmic MFMA TFLOP/s against the 2.5166 PFLOP/s dense fp16 peak (flops
 counted once: 2 x rows x K x N per product; the second activation term of the
@@ -63,8 +66,9 @@ PREFILL_SRCS = DOWN_OP_SRCS + (os.path.join(CSRC, "router.hip"),)
 BATCH_SRCS = tuple(os.path.join(CSRC, f) for f in ("skinny_gemm.hip", "route_small.hip",
                                                    "mfma_frag.hpp", "ffn_generic.hip"))
 STACK_LAYERS_PER_LAUNCH = 24
-WORKLOADS = ("toy", "decode_per_layer", "decode_batch", "prefill_down", "prefill_stack")
-CPU_BUDGET = {"toy": 2.0, "decode_batch": 6.0, "prefill_down": 6.0, "prefill_stack": 15.0}
+WORKLOADS = ("toy", "decode_per_layer", "decode_batch", "prefill_down", "prefill_stack", "attn_prep")
+CPU_BUDGET = {"toy": 2.0, "decode_batch": 6.0, "prefill_down": 6.0, "prefill_stack": 15.0,
+              "attn_prep": 3.0}
 
 
 def parse():
@@ -414,6 +418,49 @@ def bench_prefill_stack(torch, M, S, dev, stream, arena, layers_np, gates, iters
     return r
 
 
+def bench_attn(torch, M, S, dev, stream, iters, cpu):
+    """One decode token through the attention-side primitives, 48 distinct layers."""
+    from oracle import moe_oracle as O
+    Dm, nq, nkv, hd, L = 2048, 32, 4, 128, 48
+    N = S.qkv_rows(nq, nkv, hd)
+    arena = S.device_qkv_arena(6, L, Dm, nq, nkv, hd, S.FMT_Q8_0, dev)
+    gnp = [S.attn_gain(6, Dm, 0), S.attn_gain(6, hd, 1), S.attn_gain(6, hd, 2)]
+    ga, gq, gk = (torch.from_numpy(g).to(dev) for g in gnp)
+    W = [M.AttnWeights(arena[l], ga, gq, gk, Dm, nq, nkv, hd, S.FMT_Q8_0) for l in range(L)]
+    max_pos = 8192
+    x = torch.from_numpy(S.hidden(6, 1, Dm)).to(dev)
+    pos = torch.tensor([4097], dtype=torch.int32, device=dev)
+    q = torch.empty((1, nq, hd), dtype=torch.float32, device=dev)
+    kc = torch.zeros((L, max_pos, nkv, hd), dtype=torch.float32, device=dev)
+    vc = torch.zeros((L, max_pos, nkv, hd), dtype=torch.float32, device=dev)
+    ws = M.attn_workspace(1, W[0])
+
+    def one():
+        for l in range(L):
+            M.moe_attn_prep(x, W[l], pos, q, kc[l], vc[l], ws=ws, stream=stream)
+    ms = graph_time_ms(torch, one, stream, 3, iters) / L
+    rb = Dm // 32 * 34
+    nbytes = N * rb + Dm * 4 * 2 + 2 * hd * 4 + nq * hd * 4 + 2 * nkv * hd * 4 + 4
+    r = {"workload": "attention-side primitives, one decode token: input RMSNorm, Q8_0 Q/K/V "
+                     "projection 2048 -> (32 + 4 + 4) x 128, per-head Q/K RMSNorm, RoPE, F32 KV "
+                     "append; 48 distinct layers",
+         "us_per_call": round(ms * 1e3, 3)}
+    r.update(rates(ms, nbytes, 2.0 * Dm * N))
+    if cpu:
+        xnp = S.hidden(6, 1, Dm)
+
+        def run(n):
+            raw = arena[n % L].cpu().numpy()
+            t0 = time.perf_counter()
+            O.attn_prep(xnp, raw, S.FMT_Q8_0, gnp[0], gnp[1], gnp[2], [4097], 1e6, nq, nkv, hd)
+            return time.perf_counter() - t0
+        r["cpu_baseline"] = oracle_rate(run, CPU_BUDGET["attn_prep"], 100, 1, "tokens/s",
+                                        "{n} single-token calls of the fp64 oracle (dequantising "
+                                        "the 5120 x 2048 Q8_0 projection, norms, RoPE); {s:.1f} s")
+    del arena, kc, vc
+    return r
+
+
 def lazy_layer(arena_l):
     """The oracle's Experts over one Q8_0 layer of a device arena, bytes fetched per expert."""
     import moe_synth as S
@@ -545,6 +592,10 @@ def main():
         extra["prefill_stack"] = bench_prefill_stack(torch, M, S, dev, stream, arena, layers_np,
                                                      gates, max(2, iters // 4), cpu)
         print(f"[bench] prefill_stack: {extra['prefill_stack']['ms_per_pass']:.3f} ms per pass",
+              file=sys.stderr, flush=True)
+    if "attn_prep" in want:
+        extra["attn_prep"] = bench_attn(torch, M, S, dev, stream, iters, cpu)
+        print(f"[bench] attn_prep: {extra['attn_prep']['us_per_call']:.2f} us per token-layer",
               file=sys.stderr, flush=True)
     if extra:
         line["workloads"] = extra

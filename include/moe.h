@@ -253,6 +253,53 @@ moe_status moe_decode_stack(const float* x, int32_t num_layers,
                             float* outs, int32_t* topk_ids, float* topk_w, void* ws,
                             size_t ws_bytes, void* stream);
 
+/* Attention-side weights of one layer (host struct holding device pointers)
+ * for moe_attn_prep. */
+typedef struct {
+  int32_t d_model;          /* D: multiple of 32, at most 3584                          */
+  int32_t n_q_heads;        /* Hq >= 1                                                   */
+  int32_t n_kv_heads;       /* Hkv >= 1                                                  */
+  int32_t head_dim;         /* hd: multiple of 16, at most 256                           */
+  int32_t format;           /* MOE_FMT_* of w_qkv                                        */
+  const void* w_qkv;        /* (Hq + 2 Hkv) * hd stored rows of D/32 blocks: the q rows
+                               of head 0..Hq-1, then the k rows of head 0..Hkv-1, then
+                               the v rows (row n = output n); 16-byte aligned           */
+  const float* attn_gain;   /* [D] gain of the input RMSNorm; 16-byte aligned            */
+  const float* q_gain;      /* [hd] gain of the per-head q RMSNorm                       */
+  const float* k_gain;      /* [hd] gain of the per-head k RMSNorm                       */
+} moe_attn_weights;
+
+/* Bytes of workspace moe_attn_prep needs: 256 header bytes (the error word
+ * at byte 64, as in every workspace; read it with moe_workspace_status), the
+ * projected q and k rows of every token as tagged 64-bit words (rounded up to
+ * 256 bytes), then ceil(T/8) * (Hq + Hkv) u32 counters; 0 for T == 0 or a NULL
+ * W.  The workspace must be 256-byte aligned and zero-filled before its first
+ * use; the counters keep running across calls. */
+size_t moe_attn_workspace_bytes(int64_t T, const moe_attn_weights* W /* host */);
+
+/* The attention-side primitives of the warm decode path (technical-overview
+ * page, "Validated GPU foundation": RMSNorm, grouped per-head Q/K
+ * normalization, Q/K/V projections, RoPE, request-local F32 KV append).  For
+ * each token t:
+ *   u = x_t / sqrt(mean(x_t^2) + eps) * attn_gain;
+ *   [q | k | v] = u W_qkv (block-quantized rows, fp32 accumulation);
+ *   every q head: q_h / sqrt(mean(q_h^2) + eps) * q_gain, every k head likewise
+ *   with k_gain (one shared gain per kind, the grouped per-head norm);
+ *   RoPE on q and k: for i < hd/2 the pair (e_i, e_{i+hd/2}) is rotated by the
+ *   angle pos[t] * rope_theta^(-2i/hd);
+ *   q [T][Hq][hd] gets the rotated q; k_cache and v_cache ([max_pos][Hkv][hd]
+ *   fp32, caller-owned) get the rotated k and the projected v at row pos[t].
+ *   A token whose pos is outside [0, max_pos) writes q only.
+ * Causal attention itself (scores, softmax, value aggregation, output
+ * projection) is not part of this call.  x [T][D] 16-byte aligned; pos [T]
+ * int32; ws at least moe_attn_workspace_bytes, zero-filled before first use,
+ * not shared by calls that may overlap.  Asynchronous on `stream`; one launch;
+ * results are bit-reproducible. */
+moe_status moe_attn_prep(const float* x, int64_t T, const moe_attn_weights* W /* host */,
+                         const int32_t* pos, float rope_theta, float eps, float* q,
+                         float* k_cache, float* v_cache, int32_t max_pos, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* RMSNorm with unit gain (evidence page: "RMSNorm and residual transitions"):
  * out[t] = x[t] / sqrt(mean_D(x[t]^2) + eps).  out may equal x. */
 moe_status moe_rmsnorm(const float* x, int64_t T, int32_t D, float eps, float* out, void* stream);

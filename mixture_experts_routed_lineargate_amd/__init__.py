@@ -37,6 +37,15 @@ class moe_experts(ctypes.Structure):
     ]
 
 
+class moe_attn_weights(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("format", ctypes.c_int32),
+        ("w_qkv", ctypes.c_void_p), ("attn_gain", ctypes.c_void_p), ("q_gain", ctypes.c_void_p),
+        ("k_gain", ctypes.c_void_p),
+    ]
+
+
 class moe_stack_layer(ctypes.Structure):
     _fields_ = [("gate", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("experts", moe_experts)]
 
@@ -61,6 +70,9 @@ _SIGS = {
     "moe_workspace_status": (_I32, [_P, _SZ, _I32, _P]),
     "moe_layer_noalloc": (_I32, [_P, _P, _P, ctypes.POINTER(moe_experts), _I64, _I32, _I32, _P, _P,
                                  _P, _P, _P, _P]),
+    "moe_attn_workspace_bytes": (_SZ, [_I64, ctypes.POINTER(moe_attn_weights)]),
+    "moe_attn_prep": (_I32, [_P, _I64, ctypes.POINTER(moe_attn_weights), _P, _F32, _F32, _P, _P,
+                             _P, _I32, _P, _SZ, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -294,3 +306,44 @@ def moe_decode_stack(x, layers: StackLayers, k: int, outs, flags: int = 0, topk_
     _check("moe_decode_stack", lib().moe_decode_stack(
         _ptr(x), layers.n, layers.c, k, flags, _ptr(outs), _ptr(topk_ids), _ptr(topk_w),
         _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+class AttnWeights:
+    """One layer's attention-side weights for moe_attn_prep (keeps the tensors alive).
+
+    ``w_qkv`` uint8 device tensor of (Hq + 2 Hkv) * hd stored rows of D/32 blocks (q
+    heads, then k heads, then v heads); gains fp32 device tensors [D], [hd], [hd]."""
+
+    def __init__(self, w_qkv, attn_gain, q_gain, k_gain, D: int, n_q: int, n_kv: int,
+                 head_dim: int, fmt: int):
+        import torch
+        _need(w_qkv, torch.uint8, "w_qkv")
+        for t, n in ((attn_gain, "attn_gain"), (q_gain, "q_gain"), (k_gain, "k_gain")):
+            _need(t, torch.float32, n)
+        self.keep = (w_qkv, attn_gain, q_gain, k_gain)
+        self.n_q, self.n_kv, self.hd, self.D = n_q, n_kv, head_dim, D
+        self.c = moe_attn_weights(D, n_q, n_kv, head_dim, fmt, _ptr(w_qkv), _ptr(attn_gain),
+                                  _ptr(q_gain), _ptr(k_gain))
+
+
+def attn_workspace(T: int, W: AttnWeights, device="cuda"):
+    """Zero-filled workspace for moe_attn_prep (its arrival counters start at zero)."""
+    import torch
+    n = int(lib().moe_attn_workspace_bytes(T, ctypes.byref(W.c)))
+    return torch.zeros(max(n, 4) // 4, dtype=torch.float32, device=device)
+
+
+def moe_attn_prep(x, W: AttnWeights, pos, q, k_cache, v_cache, rope_theta: float = 1e6,
+                  eps: float = 1e-6, ws=None, stream=None):
+    """q [T][Hq][hd] <- normalised, rotated q; k_cache / v_cache [max_pos][Hkv][hd]
+    get row pos[t] (see moe.h)."""
+    import torch
+    for t, dt, n in ((x, torch.float32, "x"), (pos, torch.int32, "pos"), (q, torch.float32, "q"),
+                     (k_cache, torch.float32, "k_cache"), (v_cache, torch.float32, "v_cache"),
+                     (ws, torch.float32, "ws")):
+        _need(t, dt, n)
+    T = x.shape[0]
+    max_pos = 0 if k_cache is None else k_cache.shape[0]
+    _check("moe_attn_prep", lib().moe_attn_prep(
+        _ptr(x), T, ctypes.byref(W.c), _ptr(pos), rope_theta, eps, _ptr(q), _ptr(k_cache),
+        _ptr(v_cache), max_pos, _ptr(ws), 0 if ws is None else ws.numel() * 4, _stream(stream)))

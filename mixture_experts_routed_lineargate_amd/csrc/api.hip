@@ -505,6 +505,40 @@ moe_status moe_workspace_status(void* ws, size_t ws_bytes, int32_t reset, void* 
   return MOE_E_TIMEOUT;
 }
 
+size_t moe_attn_workspace_bytes(int64_t T, const moe_attn_weights* W) {
+  if (T <= 0 || !W || W->n_q_heads <= 0 || W->n_kv_heads <= 0 || W->head_dim <= 0) return 0;
+  const int N = (W->n_q_heads + 2 * W->n_kv_heads) * W->head_dim;
+  return attn_count_offset(T, N) +
+         (size_t)((T + 7) / 8) * (size_t)(W->n_q_heads + W->n_kv_heads) * sizeof(uint32_t);
+}
+
+moe_status moe_attn_prep(const float* x, int64_t T, const moe_attn_weights* W, const int32_t* pos,
+                         float rope_theta, float eps, float* q, float* k_cache, float* v_cache,
+                         int32_t max_pos, void* ws, size_t ws_bytes, void* stream) {
+  if (!W) return MOE_E_NULLPTR;
+  if (W->format != MOE_FMT_Q8_0 && W->format != MOE_FMT_Q4) return MOE_E_FORMAT;
+  const int D = W->d_model, Hq = W->n_q_heads, Hkv = W->n_kv_heads, hd = W->head_dim;
+  if (T < 0 || D <= 0 || D % QK || Hq <= 0 || Hkv <= 0 || hd <= 0 || hd % 16 || max_pos < 0)
+    return MOE_E_SHAPE;
+  if (D > 3584 || hd > 256 || Hq > 1024 || Hkv > 1024) return MOE_E_UNSUPPORTED;   // LDS <= 64 KB
+  if (!(rope_theta > 1.0f) || !(eps >= 0.0f)) return MOE_E_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !pos || !q || !W->w_qkv || !W->attn_gain || !W->q_gain || !W->k_gain) return MOE_E_NULLPTR;
+  if (max_pos > 0 && (!k_cache || !v_cache)) return MOE_E_NULLPTR;
+  if (!aligned(x, 16) || !aligned(W->w_qkv, 16) || !aligned(W->attn_gain, 16) ||
+      !aligned(W->q_gain, 4) || !aligned(W->k_gain, 4) || !aligned(pos, 4) || !aligned(q, 4) ||
+      (k_cache && !aligned(k_cache, 4)) || (v_cache && !aligned(v_cache, 4)))
+    return MOE_E_ALIGN;
+  const size_t need = moe_attn_workspace_bytes(T, W);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return MOE_E_WORKSPACE;
+  trace("attn prep", T, D, hd, Hq, Hkv, W->format);
+  if (launch_attn_prep(x, T, D, W->attn_gain, (const uint8_t*)W->w_qkv, W->format, Hq, Hkv, hd,
+                       W->q_gain, W->k_gain, pos, rope_theta, eps, q, k_cache, v_cache, max_pos,
+                       ws, (hipStream_t)stream) != hipSuccess)
+    return MOE_E_HIP;
+  return MOE_OK;
+}
+
 moe_status moe_rmsnorm(const float* x, int64_t T, int32_t D, float eps, float* out, void* stream) {
   if (T < 0 || D <= 0) return MOE_E_SHAPE;
   if (T == 0) return MOE_OK;

@@ -57,7 +57,11 @@ constexpr int NT = 256;               // threads per workgroup (4 wavefronts, tw
 constexpr int BN = 256;               // weight rows per tile (64 per wavefront)
 constexpr int BKB = 2;                // blocks per K chunk
 constexpr int BK = BKB * QK;          // 64 values per K chunk
-constexpr int WG_PER_CU = 2;
+// workgroups per CU (at most): two.  Three fit with single-fp16 activations and
+// 4-bit weights but measured no faster (the kernel is bound by its VALU work, not
+// by waves to hide latency with)
+template <bool SPLIT>
+constexpr int wg_per_cu() { return 2; }
 
 enum { STAGE_GATEUP = 0, STAGE_DOWN = 1 };
 
@@ -158,7 +162,7 @@ static int device_cus() {
 // with their 16-byte pieces XOR-swizzled by row, so the 16 rows a fragment
 // read touches fall in distinct banks.
 template <int FMT, int STAGE, int MSUB, bool SPLIT>
-__global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
+__global__ __launch_bounds__(NT, wg_per_cu<SPLIT>()) void grouped_gemm_kernel(Args p) {
   constexpr int BM = 16 * MSUB;
   constexpr int TW = NT / BM;                       // tiles per metadata window
   constexpr int PL = SPLIT ? 2 : 1;                 // activation planes
@@ -429,6 +433,25 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void grouped_gemm_kernel(Args p) {
   }
 }
 
+// Resident workgroups per CU of one kernel variant at its dynamic LDS size
+// (cached per device and E), at most wg_per_cu.
+template <int FMT, int STAGE, int MSUB, bool SPLIT>
+static int resident_per_cu(int E) {
+  static int cache[64][MAX_E + 1];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || E < 1 || E > MAX_E) return 1;
+  int& c = cache[dev][E];
+  if (c == 0) {
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per, grouped_gemm_kernel<FMT, STAGE, MSUB, SPLIT>, NT,
+            (size_t)2 * (E + 1) * sizeof(int)) != hipSuccess || per < 1)
+      per = 1;
+    c = per < wg_per_cu<SPLIT>() ? per : wg_per_cu<SPLIT>();
+  }
+  return c;
+}
+
 template <int FMT, int STAGE, int MSUB, bool SPLIT>
 static hipError_t launch_t(const Args& a, int64_t R, hipStream_t s) {
   constexpr int BM = 16 * MSUB;
@@ -436,7 +459,8 @@ static hipError_t launch_t(const Args& a, int64_t R, hipStream_t s) {
   int64_t grid = max_m * a.n_tiles;                // upper bound of the tile count
   const int cus = device_cus();
   if (cus <= 0) return hipErrorInvalidDevice;
-  if (grid > (int64_t)cus * WG_PER_CU) grid = (int64_t)cus * WG_PER_CU;   // persistent
+  const int W = resident_per_cu<FMT, STAGE, MSUB, SPLIT>(a.E);
+  if (grid > (int64_t)cus * W) grid = (int64_t)cus * W;   // persistent: every workgroup resident
   hipLaunchKernelGGL((grouped_gemm_kernel<FMT, STAGE, MSUB, SPLIT>), dim3((unsigned)grid), dim3(NT),
                      (size_t)2 * (a.E + 1) * sizeof(int), s, a);
   return hipGetLastError();

@@ -206,4 +206,15 @@ hipError_t launch_decode_stack(const float* x, int L, const StackLayer* layers, 
                                bool prenorm0, float* outs, int32_t* ids, float* w,
                                const Workspace& ws, hipStream_t s);
 
+// attention-side primitives (attn_prep.hip); ws: 256 header bytes (error word at 64),
+// [T][N] tagged 64-bit published rows, then (at attn_count_offset) [ceil(T/8)][Hq + Hkv]
+// u32 ticket counters; zero-filled before first use
+size_t attn_lds_bytes(int D, int fmt);
+size_t attn_count_offset(int64_t T, int N);
+hipError_t launch_attn_prep(const float* x, int64_t T, int D, const float* attn_gain,
+                            const uint8_t* w_qkv, int fmt, int Hq, int Hkv, int hd,
+                            const float* q_gain, const float* k_gain, const int32_t* pos,
+                            float theta, float eps, float* q, float* k_cache, float* v_cache,
+                            int max_pos, void* ws, hipStream_t s);
+
 }  // namespace moe

@@ -14,7 +14,10 @@ d_ff 768, 48 layers, 128 experts, learned top-8 routing) with synthetic values:
 * per-expert logit bias b_e = -s * ln(r_e), r a seeded permutation of 1..E,
   i.e. the log of a Zipf(s) popularity (the normalising constant is dropped:
   softmax and top-k ignore a shift);
-* expert matrices ~ N(0, 0.02), encoded block-wise along the reduction axis.
+* expert matrices ~ N(0, 0.02), encoded block-wise along the reduction axis;
+* attention-side inputs: Q/K/V projection rows ~ N(0, 0.02) block-encoded (q
+  rows of every head, then k, then v), norm gains 1 + N(0, 0.1), distinct
+  token positions drawn without replacement.
 
 Every generator is numpy ``default_rng(SeedSequence([SEED, cfg, layer, role,
 expert]))``.  Large weight arenas (hundreds of experts) are drawn on the GPU
@@ -43,6 +46,7 @@ import numpy as np
 SEED = 0x4D4F45  # "MOE"
 
 ROLE_X, ROLE_G, ROLE_ZIPF, ROLE_WG, ROLE_WU, ROLE_WD, ROLE_H, ROLE_REDRAW = range(8)
+ROLE_WQKV, ROLE_GAIN, ROLE_POS = 8, 9, 10
 
 FMT_Q8_0 = 0
 FMT_Q4 = 1
@@ -244,3 +248,47 @@ def device_arena(cfg: int, layers: int, E: int, D: int, F: int, fmt: int, device
             arena[l, :, off:off + nbytes] = q
             del w, q
     return arena
+
+
+# ----------------------------------------------------------------------------
+# Attention-side inputs (input / per-head norm gains, Q/K/V projection rows)
+# ----------------------------------------------------------------------------
+
+def qkv_rows(n_q: int, n_kv: int, head_dim: int) -> int:
+    return (n_q + 2 * n_kv) * head_dim
+
+
+def attn_gain(cfg: int, n: int, which: int, layer: int = 0, std: float = 0.1) -> np.ndarray:
+    """A norm gain vector, fp32 [n]: 1 + N(0, std) (which: 0 input, 1 q, 2 k)."""
+    g = generator(cfg, layer, ROLE_GAIN, which)
+    return (1.0 + g.standard_normal(n, dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def qkv_weights(cfg: int, D: int, n_q: int, n_kv: int, head_dim: int, fmt: int, layer: int = 0,
+                std: float = 0.02) -> np.ndarray:
+    """Host-drawn Q/K/V projection: uint8 [(n_q + 2 n_kv) * head_dim][D/32 * block bytes]
+    (q rows of every head, then k, then v), N(0, std) weights block-encoded."""
+    N = qkv_rows(n_q, n_kv, head_dim)
+    return quantize(normal_rows(cfg, layer, ROLE_WQKV, 0, N, D, std), fmt)
+
+
+def device_qkv_arena(cfg: int, layers: int, D: int, n_q: int, n_kv: int, head_dim: int, fmt: int,
+                     device, std: float = 0.02):
+    """Q/K/V projections of several layers drawn on ``device``: uint8 [layers][N][row bytes]."""
+    import torch
+    N = qkv_rows(n_q, n_kv, head_dim)
+    rb = D // BLOCK * BLOCK_BYTES[fmt]
+    arena = torch.empty((layers, N, rb), dtype=torch.uint8, device=device)
+    gen = torch.Generator(device=device)
+    for l in range(layers):
+        seed = int(np.random.SeedSequence([SEED, cfg, l, ROLE_WQKV]).generate_state(1, np.uint64)[0] >> 1)
+        gen.manual_seed(seed)
+        w = torch.randn((N, D), generator=gen, device=device, dtype=torch.float32) * std
+        arena[l] = _torch_quantize(w, fmt)
+        del w
+    return arena
+
+
+def positions(cfg: int, T: int, max_pos: int, layer: int = 0) -> np.ndarray:
+    """Distinct token positions in [0, max_pos), int32 [T]."""
+    return generator(cfg, layer, ROLE_POS).choice(max_pos, size=T, replace=False).astype(np.int32)

@@ -145,6 +145,33 @@ def test_layer_noalloc_validation():
     assert L.moe_workspace_bytes(64, 2048, 768, 128, 8, 1, 0) > 8 << 20
 
 
+def test_attn_prep_validation():
+    L = M.lib()
+
+    def W(**kw):
+        base = dict(d_model=2048, n_q_heads=32, n_kv_heads=4, head_dim=128, format=0,
+                    w_qkv=FAKE, attn_gain=FAKE, q_gain=FAKE, k_gain=FAKE)
+        base.update(kw)
+        return M.moe_attn_weights(**base)
+
+    def call(w=None, T=1, x=FAKE, pos=FAKE, theta=1e6, q=FAKE, ws=FAKE, wsb=1 << 30, mp=8):
+        w = W() if w is None else w
+        return L.moe_attn_prep(x, T, ctypes.byref(w), pos, theta, 1e-6, q, FAKE, FAKE, mp, ws,
+                               wsb, None)
+    assert L.moe_attn_workspace_bytes(3, ctypes.byref(W())) == 256 + 3 * 5120 * 8 + 36 * 4
+    assert call(T=0) == 0
+    assert call(w=W(format=5)) == 4
+    assert call(w=W(head_dim=100)) == 2
+    assert call(w=W(d_model=100)) == 2
+    assert call(w=W(d_model=4096)) == 6
+    assert call(w=W(head_dim=512)) == 6
+    assert call(theta=1.0) == 2
+    assert call(x=None) == 1
+    assert call(w=W(w_qkv=None)) == 1
+    assert call(x=FAKE + 4) == 3
+    assert call(wsb=100) == 5
+
+
 def test_workspace_status_validation():
     L = M.lib()
     assert L.moe_workspace_status(None, 1 << 20, 0, None) == 1
