@@ -3,7 +3,8 @@
 // first experiment": the existing compact expert grouping is reused without a
 // new routing sort.)
 //
-// One workgroup of 1024 threads.  Stability without atomics in the scatter:
+// Up to 1024 entries (or beyond the chunk-parallel kernel's limits): one
+// workgroup of 1024 threads.  Stability without atomics in the scatter:
 // inside a wavefront, lanes holding the same expert are found with one ballot
 // per expert-id bit (a wave multisplit), a lane's rank is the popcount of the
 // equal lanes below it; wave totals are scanned across the 16 wavefronts per
@@ -91,118 +92,113 @@ __global__ __launch_bounds__(GT) void group_kernel(const int32_t* __restrict__ i
   }
 }
 
-// Single pass for GT < N <= FC * GT entries and up to FE experts (the prefill
-// microbatches).  The ids stay in registers (thread t holds
-// entries c * GT + t); the per-(chunk, wavefront) counts of each expert come
-// from the same wave multisplit; one pass then turns them into exclusive
-// prefixes in (chunk, wavefront) order, expert by expert (thread 8e + c owns
-// expert e, chunk c: a serial prefix over the 16 wavefronts, then a scan over
-// the 8 chunk threads), and the expert totals are scanned into the offsets.
-// The position of entry i is offsets[e] + prefix(e, chunk, wavefront) + rank,
-// the same stable order as above.
-constexpr int FC = 8;             // chunks of GT entries
-constexpr int FE = 128;           // experts
-constexpr int FS = FC * GW + 1;   // LDS stride per expert (odd: spreads the banks)
-static_assert(FC * FE == GT, "one thread per (expert, chunk)");
+// More than one chunk (GT < N <= CMAX * GT entries, up to ME experts): one
+// workgroup per 1024-entry chunk and no exchange between them.  Every
+// workgroup counts all N entries per (chunk, expert) in LDS; plain counts
+// suffice, since the chunk index carries the order.  From them it has the
+// expert totals (hence the offsets) and, for each expert, the entries in the
+// chunks before its own.  Its own chunk then gets the wave multisplit's stable
+// ranks and a prefix over its wavefronts, so entry i lands at
+// offsets[e] + (entries of e in earlier chunks) + (in earlier wavefronts of its
+// chunk) + (in lower lanes of its wavefront): the same stable order as above.
+constexpr int CMAX = 32;          // chunks
+constexpr int ME = 256;           // experts
+static_assert(ME <= GT && ME == 4 * WAVE, "one thread per expert; the offset scan takes four per lane");
 
-__global__ __launch_bounds__(GT) void group_fast_kernel(const int32_t* __restrict__ ids, int N,
-                                                        int E, int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ rows) {
-  __shared__ int cnt[FE * FS];    // [e][c * GW + w]: count, then exclusive prefix
-  __shared__ int tot[FE];
-  __shared__ int base[FE + 1];
+__global__ __launch_bounds__(GT) void group_multi_kernel(const int32_t* __restrict__ ids, int N,
+                                                         int E, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ rows) {
+  extern __shared__ int smem[];
+  const int nch = (N + GT - 1) / GT;
+  int* cnt = smem;                // [nch][E] entries per (chunk, expert)
+  int* wcnt = cnt + nch * E;      // [GW][E] own chunk: per wavefront, then its prefix
+  int* tot = wcnt + GW * E;       // [E]
+  int* base = tot + E;            // [E] offsets
   const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
+  const int b = blockIdx.x;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
 
-  int ev[FC];
-#pragma unroll
-  for (int c = 0; c < FC; ++c) {
-    const int i = c * GT + tid;
-    ev[c] = i < N ? ids[i] : -1;
-  }
-  for (int j = tid; j < FE * FS; j += GT) cnt[j] = 0;
+  for (int j = tid; j < (nch + GW) * E; j += GT) cnt[j] = 0;
+  const int i_own = b * GT + tid;
+  const int e_own = i_own < N ? ids[i_own] : -1;
   __syncthreads();
+  for (int c0 = 0; c0 < nch; c0 += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = (c0 + u) * GT + tid;
+      v[u] = i < N ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if ((unsigned)v[u] < (unsigned)E) atomicAdd(&cnt[(c0 + u) * E + v[u]], 1);
+  }
 
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
-  int rank[FC];
-#pragma unroll
-  for (int c = 0; c < FC; ++c) {
-    const int e = ev[c];
-    const bool valid = (unsigned)e < (unsigned)E;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
-    }
-    rank[c] = __popcll(m & below);
-    if (valid && rank[c] == 0) cnt[e * FS + c * GW + wave] = __popcll(m);
+  const bool valid = (unsigned)e_own < (unsigned)E;
+  uint64_t m = __ballot(valid);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool on = valid && ((e_own >> bit) & 1);
+    const uint64_t bb = __ballot(on);
+    m &= on ? bb : ~bb;
   }
+  const int rank = __popcll(m & below);
+  if (valid && rank == 0) wcnt[wave * E + e_own] = __popcll(m);
   __syncthreads();
 
-  {
-    const int e = tid / FC, c = tid % FC;
-    int* row = cnt + e * FS + c * GW;
-    int v[GW];
-#pragma unroll
-    for (int w = 0; w < GW; ++w) v[w] = row[w];
-    int run = 0;
+  if (tid < E) {
+    const int e = tid;
+    int all = 0, before = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int x = cnt[c * E + e];
+      before += c < b ? x : 0;
+      all += x;
+    }
+    int run = before;
 #pragma unroll
     for (int w = 0; w < GW; ++w) {
-      const int x = v[w];
-      v[w] = run;
+      const int x = wcnt[w * E + e];
+      wcnt[w * E + e] = run;
       run += x;
     }
-    int incl = run;                                   // scan over the FC chunk threads of e
-#pragma unroll
-    for (int off = 1; off < FC; off <<= 1) {
-      const int o = __shfl_up(incl, off, FC);
-      if (c >= off) incl += o;
-    }
-    const int excl = incl - run;
-#pragma unroll
-    for (int w = 0; w < GW; ++w) row[w] = v[w] + excl;
-    if (c == FC - 1) tot[e] = incl;
+    tot[e] = all;
   }
   __syncthreads();
 
   if (wave == 0) {                                    // offsets: exclusive scan of the totals
-    const int a = 2 * lane < E ? tot[2 * lane] : 0;
-    const int b = 2 * lane + 1 < E ? tot[2 * lane + 1] : 0;
-    int incl = a + b;
+    int t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = 4 * lane + u < E ? tot[4 * lane + u] : 0;
+    const int sum = t[0] + t[1] + t[2] + t[3];
+    int incl = sum;
 #pragma unroll
     for (int off = 1; off < WAVE; off <<= 1) {
       const int o = __shfl_up(incl, off, WAVE);
       if (lane >= off) incl += o;
     }
-    const int excl = incl - a - b;
-    if (2 * lane < E) {
-      base[2 * lane] = excl;
-      offsets[2 * lane] = excl;
+    int run = incl - sum;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * lane + u;
+      if (e < E) {
+        base[e] = run;
+        if (b == 0) offsets[e] = run;
+      }
+      run += t[u];
     }
-    if (2 * lane + 1 < E) {
-      base[2 * lane + 1] = excl + a;
-      offsets[2 * lane + 1] = excl + a;
-    }
-    if (lane == WAVE - 1) offsets[E] = incl;
+    if (b == 0 && lane == WAVE - 1) offsets[E] = incl;
   }
   __syncthreads();
-
-#pragma unroll
-  for (int c = 0; c < FC; ++c) {
-    const int e = ev[c];
-    if ((unsigned)e < (unsigned)E)
-      rows[base[e] + cnt[e * FS + c * GW + wave] + rank[c]] = c * GT + tid;
-  }
+  if (valid) rows[base[e_own] + wcnt[wave * E + e_own] + rank] = i_own;
 }
 
 hipError_t launch_group(const int32_t* ids, int64_t N, int E, int32_t* offsets, int32_t* rows,
                         hipStream_t s) {
-  // one chunk or less: the chunked kernel has the lower fixed cost (its LDS
-  // footprint is E + GW * E words against FE * FS here)
-  if (E <= FE && N > GT && N <= (int64_t)FC * GT) {
-    hipLaunchKernelGGL(group_fast_kernel, dim3(1), dim3(GT), 0, s, ids, (int)N, E, offsets, rows);
+  if (E <= ME && N > GT && N <= (int64_t)CMAX * GT) {
+    const int nch = (int)((N + GT - 1) / GT);
+    const size_t lds = (size_t)((nch + GW) * E + 2 * E) * sizeof(int);
+    hipLaunchKernelGGL(group_multi_kernel, dim3(nch), dim3(GT), lds, s, ids, (int)N, E, offsets, rows);
     return hipGetLastError();
   }
   const size_t lds = (size_t)(E + GW * E) * sizeof(int);

@@ -318,12 +318,14 @@ def test_empty_input(toy_case):
     assert (out == 7.0).all()
 
 
-@pytest.mark.parametrize("T,k,E", [(2048, 8, 128), (1000, 8, 128), (513, 8, 100), (129, 8, 128),
+@pytest.mark.parametrize("T,k,E", [(2048, 8, 128), (1024, 8, 128), (1000, 8, 128), (513, 8, 100),
+                                   (129, 8, 128), (128, 8, 128), (4096, 8, 256), (300, 8, 257),
                                    (1, 8, 128), (77, 2, 16)])
 def test_group_large_and_invalid_ids(T, k, E):
     """Grouping against a stable argsort, with out-of-range ids (skipped).  1025 to
-    8192 entries over at most 128 experts take the single-pass kernel, the rest
-    the chunked one."""
+    32768 entries over at most 256 experts take the chunk-parallel kernel (one
+    workgroup per 1024 entries, ragged last chunk included), the rest the
+    single-workgroup one."""
     rng = np.random.default_rng(21 + T)
     p = np.exp(-1.1 * np.log(np.arange(1, E + 1)))
     p /= p.sum()
