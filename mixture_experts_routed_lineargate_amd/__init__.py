@@ -330,7 +330,7 @@ def attn_workspace(T: int, W: AttnWeights, device="cuda"):
     """Zero-filled workspace for moe_attn_prep (its arrival counters start at zero)."""
     import torch
     n = int(lib().moe_attn_workspace_bytes(T, ctypes.byref(W.c)))
-    return torch.zeros(max(n, 4) // 4, dtype=torch.float32, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def moe_attn_prep(x, W: AttnWeights, pos, q, k_cache, v_cache, rope_theta: float = 1e6,
@@ -340,10 +340,10 @@ def moe_attn_prep(x, W: AttnWeights, pos, q, k_cache, v_cache, rope_theta: float
     import torch
     for t, dt, n in ((x, torch.float32, "x"), (pos, torch.int32, "pos"), (q, torch.float32, "q"),
                      (k_cache, torch.float32, "k_cache"), (v_cache, torch.float32, "v_cache"),
-                     (ws, torch.float32, "ws")):
+                     (ws, torch.uint8, "ws")):
         _need(t, dt, n)
     T = x.shape[0]
     max_pos = 0 if k_cache is None else k_cache.shape[0]
     _check("moe_attn_prep", lib().moe_attn_prep(
         _ptr(x), T, ctypes.byref(W.c), _ptr(pos), rope_theta, eps, _ptr(q), _ptr(k_cache),
-        _ptr(v_cache), max_pos, _ptr(ws), 0 if ws is None else ws.numel() * 4, _stream(stream)))
+        _ptr(v_cache), max_pos, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))

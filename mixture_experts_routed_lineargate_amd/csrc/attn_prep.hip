@@ -12,7 +12,9 @@
 //     staged once in LDS and reused by every token; lane b of a wavefront takes
 //     block b (and b + 64, ...) of the row: fp32 products of the exact codes, one
 //     scale per block (the decode kernels' block_dot).  A single token streams
-//     the Q8_0 matrix once: the projection is HBM-bound.
+//     the Q8_0 matrix once: the projection is HBM-bound.  u sits in LDS with the
+//     16-byte pieces of each 32-value block rotated by the block index, so the
+//     64 lanes reading one piece of their own blocks hit distinct banks.
 //  2  v rows go straight to row pos of the v cache.  q and k rows are published
 //     to the workspace as 64-bit words (tag << 32 | fp32 bits, agent-scope
 //     stores, no fences: a device-scope fence writes back the whole L2 on this
@@ -61,7 +63,7 @@ constexpr int XV = DMAX / 4 / NT + 1;          // float4 loads of one token per 
 template <int FMT>
 __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];   // ROWS * RB (+16)
-  __shared__ __attribute__((aligned(16))) float xs[DMAX];          // u of the current token
+  __shared__ __attribute__((aligned(16))) float xs[DMAX];          // u of the current token, pieces rotated
   __shared__ float red[NT / WAVE];
   constexpr int BB = FMT == MOE_FMT_Q8_0 ? 34 : 18;
   constexpr int WV = (ROWS * (DMAX / QK) * 34 + 16 * NT - 1) / (16 * NT);   // 16-byte loads / thread
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
       const int c = i * NT + tid;
-      if (c < D4)
-        ((float4*)xs)[c] = make_float4(xq[i].x * inv * gq[i].x, xq[i].y * inv * gq[i].y,
+      if (c < D4)                                   // piece c & 7 of block c >> 3, rotated
+        ((float4*)xs)[c ^ ((c >> 3) & 7)] = make_float4(xq[i].x * inv * gq[i].x, xq[i].y * inv * gq[i].y,
                                        xq[i].z * inv * gq[i].z, xq[i].w * inv * gq[i].w);
     }
     __syncthreads();
@@ -138,13 +140,14 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
     for (int b = lane; b < nb; b += WAVE) {
       float xv[QK];
       float xsum = 0.f;
+      const float4* xb = (const float4*)xs + 8 * b;
 #pragma unroll
-      for (int i = 0; i < QK; i += 4) {
-        const float4 a = *(const float4*)(xs + b * QK + i);
-        xv[i + 0] = a.x;
-        xv[i + 1] = a.y;
-        xv[i + 2] = a.z;
-        xv[i + 3] = a.w;
+      for (int i = 0; i < QK / 4; ++i) {
+        const float4 a = xb[i ^ (b & 7)];
+        xv[4 * i + 0] = a.x;
+        xv[4 * i + 1] = a.y;
+        xv[4 * i + 2] = a.z;
+        xv[4 * i + 3] = a.w;
         xsum += (a.x + a.y) + (a.z + a.w);
       }
       acc0 += dec::block_dot<FMT>(lds, (uint32_t)(wave * RB + b * BB), xv, xsum);

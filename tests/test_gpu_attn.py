@@ -35,6 +35,7 @@ def run(cfg, T, D, nq, nkv, hd, fmt, pos, max_pos, theta=1e6, repeat=1):
         M.moe_attn_prep(torch.from_numpy(x).to(DEV), W, torch.from_numpy(pos).to(DEV), q,
                         kc[:max_pos], vc[:max_pos], rope_theta=theta, ws=ws)
         torch.cuda.synchronize()
+        M.check_workspace(ws)                 # raises if a head's wait gave up
         outs.append((q.cpu().numpy().copy(), kc.cpu().numpy()[:max_pos].copy(),
                      vc.cpu().numpy()[:max_pos].copy()))
     r = O.attn_prep(x, raw, fmt, ga, gq, gk, pos, theta, nq, nkv, hd)
