@@ -65,6 +65,7 @@ DOWN_OP_SRCS = tuple(os.path.join(CSRC, f) for f in ("grouped_gemm.hip", "mfma_f
 PREFILL_SRCS = DOWN_OP_SRCS + (os.path.join(CSRC, "router.hip"),)
 BATCH_SRCS = tuple(os.path.join(CSRC, f) for f in ("skinny_gemm.hip", "route_small.hip",
                                                    "mfma_frag.hpp", "ffn_generic.hip"))
+ATTN_SRCS = (os.path.join(CSRC, "attn_prep.hip"), os.path.join(CSRC, "decode_common.hpp"))
 STACK_LAYERS_PER_LAUNCH = 24
 WORKLOADS = ("toy", "decode_per_layer", "decode_batch", "prefill_down", "prefill_stack", "attn_prep")
 CPU_BUDGET = {"toy": 2.0, "decode_batch": 6.0, "prefill_down": 6.0, "prefill_stack": 15.0,
@@ -446,6 +447,8 @@ def bench_attn(torch, M, S, dev, stream, iters, cpu):
                      "append; 48 distinct layers",
          "us_per_call": round(ms * 1e3, 3)}
     r.update(rates(ms, nbytes, 2.0 * Dm * N))
+    r["algorithmic_bytes_per_call"] = nbytes
+    r["traffic"] = counter_traffic("attn_prep_q8_0", ATTN_SRCS)
     if cpu:
         xnp = S.hidden(6, 1, Dm)
 
