@@ -447,7 +447,9 @@ def bench_attn(torch, M, S, dev, stream, iters, cpu):
                      "append; 48 distinct layers",
          "us_per_call": round(ms * 1e3, 3)}
     r.update(rates(ms, nbytes, 2.0 * Dm * N))
-    r["algorithmic_bytes_per_call"] = nbytes
+    # fp32 vector dots, no matrix cores: the MFMA fields do not apply
+    r.pop("mfma_tflops", None)
+    r.pop("mfma_frac", None)
     r["traffic"] = counter_traffic("attn_prep_q8_0", ATTN_SRCS)
     if cpu:
         xnp = S.hidden(6, 1, Dm)
