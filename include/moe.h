@@ -77,8 +77,10 @@ enum {
   MOE_E_WORKSPACE = 5,   /* ws NULL or smaller than moe_workspace_bytes          */
   MOE_E_UNSUPPORTED = 6, /* limits: E > 1024, k > 32, D or F > 16384              */
   MOE_E_HIP = 7,         /* a HIP launch failed                                   */
-  MOE_E_TIMEOUT = 8      /* moe_workspace_status: a fused kernel's bounded wait   */
+  MOE_E_TIMEOUT = 8,     /* moe_workspace_status: a fused kernel's bounded wait   */
                          /* gave up since the word was last cleared               */
+  MOE_E_RANGE = 9        /* moe_workspace_status: a fused decode stack met a value */
+                         /* outside its fixed-point range (outputs hold NaN)      */
 };
 
 enum { MOE_FMT_Q8_0 = 0, MOE_FMT_Q4 = 1 };
@@ -240,7 +242,13 @@ typedef struct {
  * geometry (D 2048, F 768, E 128, k 8, every layer in one format, 16-byte
  * aligned weight bases and strides) one persistent launch runs up to 24
  * layers with no launch between them, and its fp outputs are
- * bit-reproducible.  Other shapes run moe_layer per layer.
+ * bit-reproducible: each layer's output o_l and the next router's logits are
+ * summed across workgroups in 64-bit fixed point (2^-24 resolution, exact and
+ * independent of arrival order).  There a contribution to o_l (a slot's
+ * w_j y_j(d), or the residual) must stay below 2^27 in magnitude and a
+ * 64-row partial logit below 2^13; beyond that the outputs from that layer on
+ * are NaN and moe_workspace_status reports MOE_E_RANGE.  Other shapes run
+ * moe_layer per layer.
  *   x [D] fp32 (one token); layers: host array of num_layers >= 1 entries;
  *   outs [num_layers][D] fp32: o_l of every layer;
  *   topk_ids [num_layers][k] int32, topk_w [num_layers][k] fp32: optional
@@ -308,11 +316,14 @@ moe_status moe_rmsnorm(const float* x, int64_t T, int32_t D, float eps, float* o
  * SYNCHRONOUS: waits for every call enqueued on `stream` so far, then reads
  * the u32 word at byte 64 of ws (a device pointer).  Returns MOE_OK if it is
  * zero, MOE_E_TIMEOUT if a bounded wait of any call on this workspace gave up
- * since it was last cleared (the outputs of that call hold NaN), MOE_E_HIP if
- * the copy failed, MOE_E_NULLPTR / MOE_E_WORKSPACE for a missing or too small
- * workspace (ws_bytes < 68).  With reset != 0 and a timeout recorded, the
- * exchange region (the first 4 MiB, launch counters included) is zero-filled
- * before returning, so the workspace is usable again.  Not for graph capture. */
+ * since it was last cleared (the outputs of that call hold NaN), otherwise
+ * MOE_E_RANGE if a decode stack met a value outside its fixed-point range
+ * (see moe_decode_stack; its later outputs hold NaN), MOE_E_HIP if the copy
+ * failed, MOE_E_NULLPTR / MOE_E_WORKSPACE for a missing or too small
+ * workspace (ws_bytes < 68).  With reset != 0 and an error recorded, the
+ * exchange region (the first 4 MiB: launch counters, exchange words and the
+ * decode stack's accumulators) is zero-filled before returning, so the
+ * workspace is usable again.  Not for graph capture. */
 moe_status moe_workspace_status(void* ws, size_t ws_bytes, int32_t reset, void* stream);
 
 /* Host-side helpers. */

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 
 MOE_OK = 0
 MOE_E_TIMEOUT = 8
+MOE_E_RANGE = 9
 FMT_Q8_0, FMT_Q4 = 0, 1
 STAGE_FULL, STAGE_DOWN = 0, 1
 F_RESIDUAL, F_DETERMINISTIC, F_PRENORM, F_FP16_ACT, F_BANDED = 1, 2, 4, 8, 16
@@ -233,9 +234,10 @@ def moe_layer(x, gate, bias, experts: Experts, k: int, out, flags: int = 0, topk
 
 def moe_workspace_status(ws, reset: bool = False, stream=None) -> int:
     """Status of the workspace's device-side error word (synchronous: waits for
-    ``stream``).  MOE_OK, or MOE_E_TIMEOUT when a fused kernel's bounded wait
-    gave up (its outputs hold NaN); ``reset`` zero-fills the exchange region
-    after a timeout so the workspace can be used again."""
+    ``stream``).  MOE_OK; MOE_E_TIMEOUT when a fused kernel's bounded wait gave
+    up, else MOE_E_RANGE when a decode stack met a value outside its fixed-point
+    range (the outputs hold NaN either way); ``reset`` zero-fills the exchange
+    region after an error so the workspace can be used again."""
     import torch
     _need(ws, torch.uint8, "ws")
     return int(lib().moe_workspace_status(_ptr(ws), ws.numel(), 1 if reset else 0,
@@ -243,7 +245,8 @@ def moe_workspace_status(ws, reset: bool = False, stream=None) -> int:
 
 
 def check_workspace(ws, stream=None):
-    """Raise MoeError if a fused kernel's bounded wait gave up on this workspace."""
+    """Raise MoeError if a fused kernel recorded an error on this workspace (a
+    bounded wait that gave up, or a decode-stack value out of range)."""
     st = moe_workspace_status(ws, stream=stream)
     if st != MOE_OK:
         raise MoeError("moe_workspace_status", st)

@@ -288,6 +288,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_E_UNSUPPORTED: return "shape outside supported limits";
     case MOE_E_HIP: return "HIP launch failed";
     case MOE_E_TIMEOUT: return "a bounded exchange wait gave up (outputs hold NaN)";
+    case MOE_E_RANGE: return "a decode-stack value outside the fixed-point range (outputs hold NaN)";
     default: return "unknown status";
   }
 }
@@ -502,7 +503,7 @@ moe_status moe_workspace_status(void* ws, size_t ws_bytes, int32_t reset, void* 
     if (hipMemsetAsync(ws, 0, n, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
       return MOE_E_HIP;
   }
-  return MOE_E_TIMEOUT;
+  return (word & 1u) ? MOE_E_TIMEOUT : MOE_E_RANGE;
 }
 
 size_t moe_attn_workspace_bytes(int64_t T, const moe_attn_weights* W) {

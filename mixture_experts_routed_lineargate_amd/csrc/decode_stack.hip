@@ -9,46 +9,77 @@
 // page: warm target path router -> resident expert -> combine).
 //
 // Work split (decode_common.hpp): workgroup w serves expert slot j = w / 32,
-// part r = w % 32 (24 gate/up rows, 64 down rows of the selected expert).  The
-// 64 router workgroups (eg, ds) = (w % 8, w / 8) also own the 256-row slice ds
-// of the residual stream.  Per layer l:
-//  R  router workgroup (eg, ds): gather w_j y_j(d) of layer l-1 for its slice
-//     (8 words per row, from the 32 workgroups whose down rows cover it), sum
-//     them in slot order onto the residual in_{l-1}(d): that is o_{l-1}(d),
-//     bit-identical in the 8 workgroups of the slice.  Publish o_{l-1}(d) for
-//     32 rows (the broadcast copy, 32 replicas), the partial logits of 16
-//     experts over the slice, and the slice's sum of squares.
-//  S  every workgroup: gather the partials and sums of squares, form
-//     inv = 1/rms, logits = inv * sum_ds partial + bias, top-8 and weights.
-//     The o broadcast is read in the same round as the partials and waited
-//     for before any weight load leaves the workgroup: queued behind the
-//     weight stream, its latency would be that of the whole stream.
+// part r = w % 32: 24 gate/up rows and the 64 down rows d = 64r .. 64r+63 of
+// the selected expert.  Per layer l:
+//  S  every workgroup: gather o_{l-1} (x for l = 0) and z_l = G_l^T o_{l-1};
+//     Σ o^2 by a block reduction (every workgroup forms the same inv = 1/rms
+//     from the same values in the same order), logits = inv * z_l + bias,
+//     top-8 and weights.  o is read and waited for before any weight load
+//     leaves the workgroup: queued behind the weight stream, its latency would
+//     be that of the whole stream.
 //  W  stream the weight share of the selected expert (~153 KB for Q8_0)
 //     through registers, the (gate, up) row groups two ahead of
 //  H  the gate/up dots (x = in_l = inv * o); publish h_j(f).  Then the down
-//     rows and the next layer's gate rows and bias.
-//  Y  gather h_j (768 values), the 64 down rows, publish w_j y_j(d).
-// Layer 0 runs the same steps with o_{-1} = x (inv = 1 unless the stack
-// continues an earlier one).  After the last layer the router workgroups
-// gather y once more and write the last output.  Three exchanges sit on each layer's critical path
-// (y -> R, R -> S, H -> Y).
+//     rows and the next layer's gate entries and bias.
+//  Y  gather h_j (768 values), the 64 down rows: u_j(d) = w_j y_j(d).
+//  O  add u_j(d) (slot 0 also in_l(d)) into the accumulator of o_l(d), and
+//     the workgroup's share of z_{l+1} = G_{l+1}^T o_l — sum over its 64 rows
+//     of G_{l+1}(d, e) u_j(d) (slot 0: of in_l(d) + u_0(d)) — into the
+//     accumulator of z_{l+1}(e).
+// Two exchanges sit on each layer's critical path: h (H -> Y), and the
+// accumulators (O -> S).
 //
-// Exchange buffers are reused by every layer.  A buffer is rewritten for layer
-// l+1 only after its layer-l readers are done, because every publication of
-// layer l+1 depends (through the chain of exchanges) on a value that every
-// workgroup published after its own layer-l read of that buffer.
+// Accumulators.  Every layer of a launch has its own: o_l(d) receives 8
+// contributions (one per slot); z_l(e) is kept as 8 partial sums (copy c takes
+// the 32 workgroups of slot c; for layer 0, whose z = G_0^T x comes from the 32
+// slot-0 workgroups before the first layer, copy c takes the 4 with part % 8 ==
+// c), so that no word takes more than 32 adds: hundreds of adds to one word
+// queue behind each other for microseconds.  A contribution is a 64-bit
+// fetch-add of (rint(v * 2^24) << c) + 1, c = 8 (o) or 12 (z): a fixed-point
+// sum with its own count in the low bits, exact and independent of arrival
+// order, so the results are bit-reproducible.  An invalid contribution (NaN
+// after a wait that gave up, or out of range) adds 2^4 (o) or 2^6 (z) more,
+// and a sum with any such part finishes as NaN, so a failure anywhere in a
+// launch reaches every later output.  Wavefront 0 adds the o rows and
+// wavefronts 1 and 2 the z share, so the two kinds of adds are in flight
+// together.  The add that brings the count to its total returns the whole sum:
+// that lane decodes it and publishes it (o_l(d) into 32 replicas and into outs,
+// a z copy into 32 replicas) as tagged words; the reader sums the 8 z copies
+// in copy order.  A contribution to o must stay below 2^27 in magnitude and a
+// workgroup's z share below 2^22, so that the sums fit their fields; beyond
+// that it counts as invalid and sets bit 1 of the workspace's error word.
+// Accumulators start a launch at zero: at its end every workgroup zeroes its
+// share of those it used (all of their adds are done once it has passed the
+// last layer's S step), except the last layer's o words, which the lane
+// completing each one zeroes.
+//
+// Replicated words: published values are copied so that no cache line is
+// polled by more than 8 workgroups (coherent reads of one line from hundreds
+// of CUs serialise).  Tags are the launch counter + layer + 1, as for h.
 #include "decode_common.hpp"
 
 namespace moe {
 namespace dec {
 
 constexpr int LMAX = 24;        // layers per launch (per-layer pointers ride in the kernel arguments)
-constexpr int AREP = 32;        // replicas of the o broadcast
-constexpr int XB_ROW = E + 8;   // [E partial logits][sum of squares][pad]
-constexpr int OSUB = SLICE / REG;   // o rows each router workgroup broadcasts (32)
-static_assert(OSUB * AREP == 2 * NT, "two broadcast stores per thread");
-static_assert(PREP % REG == 0, "sum-of-squares replicas split evenly");
-static_assert(D == 4 * NT, "four broadcast words per thread");
+constexpr int AREP = 32;        // replicas of o
+constexpr int ZREP = 32;        // replicas of the z copies
+constexpr int ZC = 8;           // partial copies of z
+// Low fields of an accumulator word: a count of contributions (4 bits for o's
+// 8, 6 for a z copy's 32) and above it a count of invalid ones; the
+// fixed-point sum sits above both.
+constexpr int OP = 4, OQ = 8;   // o: count bits, count + invalid-count bits
+constexpr int ZP = 6, ZQ = 12;  // z copy
+constexpr int ZROWS = DPW / (NT / E);   // rows of one thread's z share (16)
+constexpr int ZT0 = WAVE;       // threads ZT0 .. ZT0 + E - 1 add the z share (wavefronts 1, 2)
+constexpr float O_LIM = 134217728.0f;   // |contribution| < 2^27: 9 of them * 2^51 < 2^55
+constexpr float Z_LIM = 4194304.0f;     // |contribution| < 2^22: 32 of them * 2^46 = 2^51
+static_assert(D == 4 * NT, "four o words per thread");
+static_assert(NT % E == 0 && DPW % (NT / E) == 0, "z shares");
+static_assert(ZC == K && PARTS % ZC == 0, "z copies: one per slot, or part % 8 for layer 0");
+static_assert(K < (1 << OP) && K < (1 << (OQ - OP)) && PARTS < (1 << ZP) &&
+              PARTS < (1 << (ZQ - ZP)), "count fields");
+static_assert(DPW <= WAVE && ZT0 + E <= NT, "o adds on wavefront 0, z adds on the next two");
 
 struct LayerPtrs {
   const float* gate;     // [D][E] fp32
@@ -64,61 +95,116 @@ struct StackArgs {
   float* outs;           // [L][D] o_l
   int32_t* ids;          // [L][K] or null
   float* w;              // [L][K] or null
-  uint64_t* xb;          // [PREP][RDS][XB_ROW] partial logits + sums of squares
-  uint64_t* xa;          // [AREP][D] o broadcast
+  uint64_t* xa;          // [AREP][D] o replicas
+  uint64_t* xz;          // [ZREP][ZC][E] replicas of the z copies
   uint64_t* xc;          // [HREP][K][F] h
-  uint64_t* xd;          // [K][D] w_j y_j
+  uint64_t* oacc;        // [LMAX][D] o accumulators (zero at launch start)
+  uint64_t* zacc;        // [LMAX][ZC][E] z accumulators (zero at launch start)
   uint32_t* epochs;      // [NWG] launch counters
-  uint32_t* err;         // poll timeout flag
+  uint32_t* err;         // bit 0: a poll timed out; bit 1: a value outside the fixed-point range
   int L;
   int prenorm0;
   LayerPtrs layer[LMAX];
 };
 
+// v * 2^24, rounded, when |v| < lim; otherwise (NaN included) 0, `bad` set and
+// the range bit of the error word raised
+__device__ inline int64_t fixq(float v, float lim, bool& bad, uint32_t* err) {
+  if (!(fabsf(v) < lim)) {
+    __hip_atomic_fetch_or(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bad = true;
+    return 0;
+  }
+  return (int64_t)__builtin_rintf(v * 16777216.0f);
+}
+
+// Add a contribution to accumulator *a (count in the low `pbits` bits, invalid
+// contributions counted above it, the sum above `qbits`).  Returns true for the
+// add that brings the count to `total`, with the finished value (NaN if any
+// contribution was invalid).
+__device__ inline bool accumulate(uint64_t* a, int64_t q, bool bad, int pbits, int qbits,
+                                  uint32_t total, float& out) {
+  const uint64_t add = ((uint64_t)q << qbits) + 1u + (bad ? (1ull << pbits) : 0ull);
+  const uint64_t old = __hip_atomic_fetch_add(a, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((uint32_t)(old & ((1ull << pbits) - 1u)) != total - 1u) return false;
+  const uint64_t sum = old + add;
+  const bool invalid = ((sum >> pbits) & ((1ull << (qbits - pbits)) - 1u)) != 0;
+  out = invalid ? __builtin_nanf("")
+                : (float)((double)((int64_t)sum >> qbits) * (1.0 / 16777216.0));
+  return true;
+}
+
 template <int FMT>
 __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
   using G = Geo<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES + 16];  // +16: reads may pass a row end by 2 bytes
-  __shared__ float red[NT];
-  __shared__ float slice_o[SLICE];
-  __shared__ float rsum[REPG];
   __shared__ float ssred[NWAVE];
   __shared__ __attribute__((aligned(16))) float lg[E];
   __shared__ __align__(16) int top[K];
   __shared__ int sel_e[K];
   __shared__ float sel_w[K];
   __shared__ float s_inv;
+  __shared__ float us[DPW];                 // u_j(d) of this workgroup's rows
+  __shared__ float vs[DPW];                 // what its z share multiplies
+  __shared__ float zred[NT / E][E];
 
   const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
   const int wg = blockIdx.x;
   const int slot = wg / PARTS, part = wg % PARTS;
-  const bool router = wg < RW;
-  const int eg = wg % REG, ds = (wg % RW) / REG;
-  const int el = tid % REPG, rg = tid / REPG;
   const int f0 = part * FPW, dr0 = part * DPW;
+  const int ze = tid % E, zq = tid / E;     // z share: expert ze over rows dr0 + 16 zq .. + 15
   uint32_t budget = SPIN_LIMIT;
   const uint32_t base = __hip_atomic_load(p.epochs + wg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int L = p.L;
 
-  // router state: thread t < SLICE owns row d = ds*SLICE + t of the residual stream
-  float o_reg = 0.f;    // o_{l-1}(d); x(d) before layer 0
-  float in_reg = 0.f;   // in_{l-1}(d)
-  if (router && tid < SLICE) o_reg = p.x[ds * SLICE + tid];
-  // Gate rows and bias of the current layer.  Every workgroup loads them (the
-  // non-router ones re-read a router workgroup's rows and drop them):
-  // conditional loads would make later waits drain the weight stream too.
-  // The bias is kept as loaded (the gate's first values stand in for a missing
-  // one) and masked where the logits are formed: using a load right away would
-  // make the compiler wait for it, and with it for every weight load before it.
-  float gq[RROWS];
+  // Gate entries of the z share and the bias of the coming layer.  Every
+  // workgroup loads them (uniform, unconditional loads keep the compiler's wait
+  // counts exact).  The bias is kept as loaded (the gate's first values stand in
+  // for a missing one) and masked where the logits are formed: using a load
+  // right away would make the compiler wait for it, and with it for every weight
+  // load before it.
+  float gq[ZROWS];
   float b0, b1;
+  auto load_gate = [&](const float* Gm, int zq_, int ze_) {
+#pragma unroll
+    for (int i = 0; i < ZROWS; ++i) gq[i] = Gm[(int64_t)(dr0 + ZROWS * zq_ + i) * E + ze_];
+  };
   {
     const LayerPtrs& l0 = p.layer[0];
-#pragma unroll
-    for (int r = 0; r < RROWS; ++r) gq[r] = l0.gate[(int64_t)(ds * SLICE + rg * RROWS + r) * E + eg * REPG + el];
+    load_gate(l0.gate, zq, ze);
     const float* bp = l0.bias ? l0.bias : l0.gate;
     b0 = bp[lane];
     b1 = bp[lane + WAVE];
+  }
+
+  // z share: the fp32 values in vs (64 rows) times the gate entries, each
+  // thread over 16 rows, then the four row quarters summed in a fixed order;
+  // z_partial ends with a barrier, z_add runs on threads ZT0 .. ZT0 + E - 1
+  auto z_partial = [&](int zq_, int ze_) {
+    float zp = 0.f;
+#pragma unroll
+    for (int i = 0; i < ZROWS; ++i) zp = fmaf(gq[i], vs[ZROWS * zq_ + i], zp);
+    zred[zq_][ze_] = zp;
+    __syncthreads();
+  };
+  auto z_add = [&](int e, int ml, int copy, uint32_t total, uint32_t tag) {
+    float z = zred[0][e];
+#pragma unroll
+    for (int q = 1; q < NT / E; ++q) z += zred[q][e];
+    bool bad = false;
+    const int64_t q = fixq(z, Z_LIM, bad, p.err);
+    float zf = 0.f;
+    if (accumulate(p.zacc + ((int64_t)ml * ZC + copy) * E + e, q, bad, ZP, ZQ, total, zf)) {
+#pragma unroll 4
+      for (int rep = 0; rep < ZREP; ++rep) publish(p.xz + (rep * ZC + copy) * E + e, tag, zf);
+    }
+  };
+  // z_0 = G_0^T x, added by the slot-0 workgroups over their rows
+  if (slot == 0) {
+    if (tid < DPW) vs[tid] = p.x[dr0 + tid];
+    __syncthreads();
+    z_partial(zq, ze);
+    if (tid >= ZT0 && tid < ZT0 + E) z_add(tid - ZT0, 0, part % ZC, PARTS / ZC, base + 1u);
   }
 
   for (int l = 0; l < L; ++l) {
@@ -128,123 +214,82 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
     // exchange addresses) live across the whole layer and spills
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const int lane = tid % WAVE, wave = tid / WAVE, el = tid % REPG, rg = tid / REPG;
+    const int lane = tid % WAVE, wave = tid / WAVE, ze = tid % E, zq = tid / E;
     const LayerPtrs& lp = p.layer[l];
 
-    // ---- R: o_{l-1} of this slice, partial logits, publish ----
-    if (router) {
-      if (l > 0 && tid < SLICE) {
-        const int d = ds * SLICE + tid;
-        float yv[K];
-        gather<K>(p.xd + d, D, t - 1u, p.err, budget, yv);
-        float s = in_reg;
-#pragma unroll
-        for (int j = 0; j < K; ++j) s += yv[j];
-        o_reg = s;
-        if (tid / OSUB == eg) p.outs[(int64_t)(l - 1) * D + d] = s;
-      }
-      float sq = 0.f;
-      if (tid < SLICE) {
-        slice_o[tid] = o_reg;
-        sq = o_reg * o_reg;
-      }
-      sq = wave_sum(sq);
-      if (lane == 0) ssred[wave] = sq;
-      __syncthreads();
-      float acc = 0.f;
-#pragma unroll
-      for (int r = 0; r < RROWS; ++r) acc = fmaf(slice_o[rg * RROWS + r], gq[r], acc);
-      red[tid] = acc;
-      // the broadcast copy of o goes out first: consumers read it after the partials
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int q = tid + i * NT;
-        const int rep = q / OSUB, dd = q % OSUB;
-        publish(p.xa + rep * D + ds * SLICE + eg * OSUB + dd, t, slice_o[eg * OSUB + dd]);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // red[g*16 + e]: lane l sums row groups l/16, l/16 + 4, ... for expert l%16,
-        // then the four lane quarters are added
-        float sum = 0.f;
-#pragma unroll
-        for (int g = 0; g < RGRP / 4; ++g) sum += red[(4 * g + (lane >> 4)) * REPG + (lane & 15)];
-        sum += __shfl_xor(sum, 32);
-        sum += __shfl_xor(sum, 16);
-        if (lane < REPG) rsum[lane] = sum;
-      }
-      __syncthreads();
-      {
-        const int rep = tid / REPG;
-        publish(p.xb + (rep * RDS + ds) * XB_ROW + eg * REPG + el, t, rsum[el]);
-      }
-      if (tid < PREP / REG) {
-        float ss = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) ss += ssred[w];
-        const int rep = eg + REG * tid;
-        publish(p.xb + (rep * RDS + ds) * XB_ROW + E, t, ss);
-      }
-    }
-
-    // ---- S: logits, top-8, weights ----
-    // Every thread polls its share of the o broadcast (wavefront 0 together with
-    // the partials and sums of squares).  The o reads complete before any weight
-    // load leaves the workgroup: queued behind the weight stream, their latency
-    // would be that of the whole stream.
-    const uint64_t* xbrep = p.xb + (wg % PREP) * RDS * XB_ROW;
+    // ---- S: o_{l-1} (x before layer 0), z_l, inv, logits, top-8, weights ----
+    // Wavefront 0 polls the 8 z copies of its two experts with its share of o
+    // (spreading the copies over the wavefronts measured slower).
     const uint64_t* arep = p.xa + (wg % AREP) * D;
+    const uint64_t* zrep = p.xz + (wg % ZREP) * ZC * E;
     float xo[4];
-    if (wave == 0) {
-      // partials [ds][e] (e = lane, lane + 64), the sum of squares of slice lane % 8,
-      // and this thread's four o words, in one poll loop
-      float pv[2 * RDS + 1 + 4];
-      gather_fn<2 * RDS + 1 + 4>(
-          [=](int i) {
-            return i < 2 * RDS ? xbrep + (i >> 1) * XB_ROW + lane + (i & 1) * WAVE
-                 : i == 2 * RDS ? xbrep + (lane % RDS) * XB_ROW + E
-                                : arep + tid + (i - 2 * RDS - 1) * NT;
-          },
-          t, p.err, budget, pv);
+    float zv[2] = {0.f, 0.f};
+    {
+      float pv[2 * ZC + 4];
+      if (wave == 0) {
+        if (l == 0)
+          gather_fn<2 * ZC>([=](int i) { return zrep + (i >> 1) * E + lane + (i & 1) * WAVE; },
+                            t, p.err, budget, pv);
+        else
+          gather_fn<2 * ZC + 4>(
+              [=](int i) {
+                return i < 2 * ZC ? zrep + (i >> 1) * E + lane + (i & 1) * WAVE
+                                  : arep + tid + (i - 2 * ZC) * NT;
+              },
+              t, p.err, budget, pv);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xo[i] = pv[2 * RDS + 1 + i];
-      float ss = 0.f;
-#pragma unroll
-      for (int s = 0; s < RDS; ++s) ss += readlane(pv[2 * RDS], s);
-      const float inv = (l > 0 || p.prenorm0) ? 1.0f / sqrtf(ss / (float)D + PRENORM_EPS) : 1.0f;
-      float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-      for (int s = 0; s < RDS; ++s) {
-        v0 += pv[2 * s];
-        v1 += pv[2 * s + 1];
+        for (int c = 0; c < ZC; ++c) {             // the copies in copy order
+          zv[0] += pv[2 * c];
+          zv[1] += pv[2 * c + 1];
+        }
       }
-      const float bm = lp.bias ? 1.f : 0.f;
-      lg[lane] = fmaf(v0, inv, b0 * bm);
-      lg[lane + WAVE] = fmaf(v1, inv, b1 * bm);
-      if (lane < K) top[lane] = -1;
-      if (lane == 0) s_inv = inv;
-    } else {
-      gather_fn<4>([=](int i) { return arep + tid + i * NT; }, t, p.err, budget, xo);
+      if (l == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xo[i] = p.x[tid + i * NT];
+      } else if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xo[i] = pv[2 * ZC + i];
+      } else {
+        gather_fn<4>([=](int i) { return arep + tid + i * NT; }, t, p.err, budget, xo);
+      }
     }
     // o lands in LDS unscaled (inv is known after the barrier); it aliases the
     // gate/up region, which is free until the group stores
     float* xs = (float*)lds;
+    float sq = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xs[tid + i * NT] = xo[i];
+    for (int i = 0; i < 4; ++i) {
+      xs[tid + i * NT] = xo[i];
+      sq = fmaf(xo[i], xo[i], sq);
+    }
+    sq = wave_sum(sq);
+    if (lane == 0) ssred[wave] = sq;
+    __syncthreads();
+    if (wave == 0) {
+      float ss = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) ss += ssred[w];
+      const float inv = (l > 0 || p.prenorm0) ? 1.0f / sqrtf(ss / (float)D + PRENORM_EPS) : 1.0f;
+      const float bm = lp.bias ? 1.f : 0.f;
+      lg[lane] = fmaf(zv[0], inv, b0 * bm);
+      lg[lane + WAVE] = fmaf(zv[1], inv, b1 * bm);
+      if (lane < K) top[lane] = -1;
+      if (lane == 0) s_inv = inv;
+    }
     __syncthreads();
     select_top8_block(lg, top, sel_e, sel_w);
     const float inv = s_inv;
     const int e_j = min(max(sel_e[slot], 0), E - 1);
     const float w_j = sel_w[slot];
-    if (router && tid < SLICE) in_reg = o_reg * inv;
-
+    // in_l over this part's rows: slot 0 adds it to o_l
+    const float in_row = (slot == 0 && tid < DPW) ? xs[dr0 + tid] * inv : 0.f;
     // ---- W + H: stream the weight share two groups ahead of the gate/up dots ----
     // A CU cannot have its whole ~153 KB share in flight: issuing it all at
     // once stalls every wavefront at the issue until most of it has arrived,
     // and the dots would only start after the stream.  So the (gate, up) row
     // groups are issued two ahead of the dots, then the down rows, then the
-    // next layer's gate rows and bias.  All loads are unconditional (clamped),
-    // which keeps the compiler's wait counts exact.
+    // next layer's gate entries and bias.  All loads are unconditional
+    // (clamped), which keeps the compiler's wait counts exact.
     const uint8_t* gsrc = lp.wg + (int64_t)e_j * lp.sg + (int64_t)f0 * G::GU_ROW;
     const uint8_t* usrc = lp.wu + (int64_t)e_j * lp.su + (int64_t)f0 * G::GU_ROW;
     const uint8_t* dsrc = lp.wd + (int64_t)e_j * lp.sd + (int64_t)dr0 * G::DN_ROW;
@@ -297,11 +342,9 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
       dn[it] = __builtin_nontemporal_load((const u32x4*)(dsrc + 16 * c));
     }
     {
-      // the last layer re-reads its own rows: unconditional loads, see above
+      // the last layer re-reads its own entries: unconditional loads, see above
       const LayerPtrs& nx = p.layer[min(l + 1, L - 1)];
-#pragma unroll
-      for (int r = 0; r < RROWS; ++r)
-        gq[r] = nx.gate[(int64_t)(ds * SLICE + rg * RROWS + r) * E + eg * REPG + el];
+      load_gate(nx.gate, zq, ze);
       const float* bp = nx.bias ? nx.bias : nx.gate;
       b0 = bp[lane];
       b1 = bp[lane + WAVE];
@@ -313,7 +356,7 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
       if (c < G::DN_CHUNKS) *(u32x4*)(lds + G::DN_OFF + 16 * c) = dn[it];
     }
 
-    // ---- Y: w_j y_j(d) for 64 down rows ----
+    // ---- Y: u_j(d) = w_j y_j(d) for 64 down rows ----
     __syncthreads();                                  // every wave is done with the gate/up region
     float* hs = (float*)lds;                          // h_j [F], reuses the gate/up region
     if (tid < F / 2) {
@@ -340,7 +383,35 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
         acc += block_dot_dig<FMT>(lds, G::DN_OFF + row * G::DN_ROW + b * G::BB, hd);
       }
       acc = sum8(acc);
-      if (sub == 0) publish(p.xd + slot * D + dr0 + row, t, w_j * acc);
+      if (sub == 0) us[row] = w_j * acc;
+    }
+    __syncthreads();
+
+    // ---- O: o_l and z_{l+1} accumulators ----
+    if (l + 1 < L) {
+      if (tid < DPW) vs[tid] = slot == 0 ? in_row + us[tid] : us[tid];
+      __syncthreads();
+      z_partial(zq, ze);
+    }
+    if (tid < DPW) {
+      const int d = dr0 + tid;
+      bool bad = false;
+      int64_t q = fixq(us[tid], O_LIM, bad, p.err);
+      if (slot == 0) q += fixq(in_row, O_LIM, bad, p.err);
+      float o;
+      uint64_t* acc = p.oacc + (int64_t)l * D + d;
+      if (accumulate(acc, q, bad, OP, OQ, K, o)) {
+        p.outs[(int64_t)l * D + d] = o;
+        if (l + 1 < L) {
+#pragma unroll 4
+          for (int rep = 0; rep < AREP; ++rep) publish(p.xa + rep * D + d, t + 1u, o);
+        } else {
+          // the last layer's word: no other add follows, zero it for the next launch
+          __hip_atomic_store(acc, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    } else if (l + 1 < L && tid >= ZT0 && tid < ZT0 + E) {
+      z_add(tid - ZT0, l + 1, slot, PARTS, t + 1u);
     }
     // the routing record goes out last: a store waits for its completion at the
     // next wait for a load, and here that is the next exchange
@@ -348,17 +419,20 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
       if (p.ids) p.ids[l * K + tid] = sel_e[tid];
       if (p.w) p.w[l * K + tid] = sel_w[tid];
     }
+    // every wavefront leaves the layer together: measured faster than letting
+    // the early ones start polling while the others still publish
+    __syncthreads();
   }
 
-  // ---- the last layer's output ----
-  if (router && tid < SLICE) {
-    const int d = ds * SLICE + tid;
-    float yv[K];
-    gather<K>(p.xd + d, D, base + (uint32_t)L, p.err, budget, yv);
-    float s = in_reg;
-#pragma unroll
-    for (int j = 0; j < K; ++j) s += yv[j];
-    if (tid / OSUB == eg) p.outs[(int64_t)(L - 1) * D + d] = s;
+  // Zero this workgroup's share of the accumulators the launch used: every add
+  // to o_0 .. o_{L-2} and z_0 .. z_{L-1} is done (this workgroup has read all of
+  // them), and the o_{L-1} words were zeroed by the lanes that completed them.
+  {
+    const int no = (L - 1) * D, nz = L * ZC * E;
+    for (int i = wg * NT + tid; i < no + nz; i += NWG * NT) {
+      uint64_t* a = i < no ? p.oacc + i : p.zacc + (i - no);
+      __hip_atomic_store(a, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   if (tid == 0)
     __hip_atomic_store(p.epochs + wg, base + (uint32_t)L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -404,12 +478,15 @@ hipError_t launch_decode_stack(const float* x, int L, const StackLayer* layers, 
   char* sync = (char*)ws.sync;
   a.err = ws.sync + ERR_WORD_OFF / sizeof(uint32_t);
   a.epochs = (uint32_t*)(sync + 4096);                    // [256] u32, shared with the layer kernel
-  a.xb = (uint64_t*)(sync + 65536);                       // [32][8][136] u64 (272 KiB)
-  a.xc = (uint64_t*)(sync + 65536 + 278528);              // [4][8][768] u64 (192 KiB)
-  a.xd = (uint64_t*)(sync + 65536 + 278528 + 196608);     // [8][2048] u64 (128 KiB)
-  a.xa = (uint64_t*)(sync + 65536 + 278528 + 196608 + 131072);  // [32][2048] u64 (512 KiB)
-  static_assert(65536 + 278528 + 196608 + 131072 + 524288 <= SYNC_BYTES, "sync region");
-  static_assert(dec::PREP * dec::RDS * dec::XB_ROW * 8 == 278528, "xb size");
+  a.xz = (uint64_t*)(sync + 65536);                       // [32][8][128] u64 (256 KiB)
+  a.xc = (uint64_t*)(sync + 327680);                      // [4][8][768] u64 (192 KiB)
+  a.xa = (uint64_t*)(sync + 524288);                      // [32][2048] u64 (512 KiB)
+  // the accumulators sit where no other kernel writes (the layer kernel ends at
+  // 640 KiB, the small-batch routing starts at ROUTE_SYNC_OFF)
+  a.oacc = (uint64_t*)(sync + STACK_ACC_OFF);                     // [24][2048] u64 (384 KiB)
+  a.zacc = (uint64_t*)(sync + STACK_ACC_OFF + 393216);            // [24][8][128] u64 (192 KiB)
+  static_assert(524288 + 524288 <= STACK_ACC_OFF &&
+                STACK_ACC_OFF + 393216 + 196608 <= ROUTE_SYNC_OFF, "sync region");
   a.L = L;
   a.prenorm0 = prenorm0 ? 1 : 0;
   for (int l = 0; l < L; ++l) {

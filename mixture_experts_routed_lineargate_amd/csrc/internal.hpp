@@ -115,6 +115,7 @@ int router_ksplit(int64_t T, int D);
 Workspace carve_workspace(void* base, int64_t T, int D, int F, int E, int k, int flags);
 constexpr size_t SYNC_BYTES = 4 * 1024 * 1024;  // barrier words and exchange buffers
 constexpr size_t ROUTE_SYNC_OFF = 2 * 1024 * 1024;  // small-batch routing's exchange words
+constexpr size_t STACK_ACC_OFF = 1280 * 1024;      // decode stack accumulators (written by no other kernel)
 constexpr size_t ERR_WORD_OFF = 64;                 // u32 error word (bounded wait gave up)
 constexpr size_t NOALLOC_SCRATCH_BYTES = 8u << 20;  // moe_layer_noalloc's static workspace
 

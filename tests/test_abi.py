@@ -34,10 +34,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(10):
         assert M.status_str(s) != "unknown status"
     assert M.status_str(0) == "ok"
-    assert M.status_str(9) == "unknown status"
+    assert M.status_str(10) == "unknown status"
 
 
 def test_workspace_bytes():

@@ -106,3 +106,36 @@ def test_decode_stack_q4_prenorm_crosses_launches():
     print(f"decode stack Q4: token {t}: worst per-layer max|d|/rms = {worst:.2e}", flush=True)
     del arena
     torch.cuda.empty_cache()
+
+
+def test_decode_stack_value_out_of_range_is_reported():
+    """The stack sums each layer's output and the next router's logits in 64-bit
+    fixed point.  An input value beyond that range (|x| >= 2^27 reaching the
+    residual of layer 0) is not summed silently: the outputs from that layer on
+    are NaN and moe_workspace_status reports MOE_E_RANGE (no wait times out).
+    After a reset the workspace gives the same bits as a fresh one."""
+    L = 3
+    arena = S.device_arena(5, L, E, D, F, S.FMT_Q8_0, DEV)
+    gates = cases.stack_layers(5, L, E, D, K)
+    dG = [(torch.from_numpy(G).to(DEV), torch.from_numpy(b).to(DEV)) for G, b in gates]
+    ex = [M.Experts.from_blobs(arena[l], D, F, S.FMT_Q8_0) for l in range(L)]
+    layers = M.StackLayers([g for g, _ in dG], [b for _, b in dG], ex)
+    x = S.hidden(5, 1, D)[0]
+    bad = x.copy()
+    bad[5] = np.float32(3.0e8)
+    ws = M.workspace(1, D, F, E, K, S.FMT_Q8_0, M.F_PRENORM)
+    outs = torch.zeros((L, D), dtype=torch.float32, device=DEV)
+    print("\ndecode stack: an input beyond the fixed-point range", flush=True)
+    M.moe_decode_stack(torch.from_numpy(bad).to(DEV), layers, K, outs, ws=ws)
+    torch.cuda.synchronize()
+    assert M.moe_workspace_status(ws) == M.MOE_E_RANGE
+    o = outs.cpu().numpy()
+    assert np.isnan(o[0]).any() and np.isnan(o[1:]).all(), "out-of-range input gave finite outputs"
+    assert M.moe_workspace_status(ws, reset=True) == M.MOE_E_RANGE
+    assert M.moe_workspace_status(ws) == M.MOE_OK
+    got, _, _ = run_stack(x, dG, ex, 0, ws)
+    fresh, _, _ = run_stack(x, dG, ex, 0, M.workspace(1, D, F, E, K, S.FMT_Q8_0, M.F_PRENORM))
+    assert np.isfinite(got).all()
+    assert np.array_equal(got.view(np.uint32), fresh.view(np.uint32)), "reset workspace differs"
+    del arena
+    torch.cuda.empty_cache()
