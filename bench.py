@@ -573,7 +573,7 @@ def main():
         M.check_workspace(ws, stream=stream)
         diff = float((bufs[L][0] - outs[L - 1]).abs().max() / outs[L - 1].pow(2).mean().sqrt())
         extra["decode_per_layer"] = {
-            "workload": "the same 48-layer step as 48 moe_layer calls (decode_layer_kernel<Q8_0>)",
+            "workload": "the same 48-layer step as 48 moe_layer calls (decode_stack_kernel<Q8_0>, one layer per launch)",
             "tokens_per_s": round(L / (ms_pl / 1e3), 1),
             "us_per_layer": round(ms_pl * 1e3 / L, 3),
             "hbm_gbps": round(DECODE_ALGO_BYTES / (ms_pl / 1e3 / L) / 1e9, 1),

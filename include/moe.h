@@ -163,9 +163,7 @@ moe_status moe_group(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
  * accuracy), or as one fp16 rounding with MOE_F_FP16_ACT; |activations| must
  * stay below 65504.  Other shapes take generic fp32 kernels.
  * Combine: the grouped kernels store y and the weighted sum runs over it in j
- * order (bit-reproducible); the generic kernels do the same.  The fused
- * single-token path adds w*y into `out` with fp32 atomics unless
- * MOE_F_DETERMINISTIC is set.
+ * order (bit-reproducible); the generic kernels do the same.
  *   stage MOE_STAGE_FULL: in = x [T][D]; for row r = t*k + j with e = ids[t][j]:
  *     h = silu(x_t W_gate_e) * (x_t W_up_e), y_r = h W_down_e.
  *   stage MOE_STAGE_DOWN: in = h [T*k][F]; y_r = h_r W_down_e (the routed
@@ -195,7 +193,11 @@ moe_status moe_combine(const float* y, const float* topk_w, int64_t T, int32_t k
  *   (the RMSNorm transition between stacked layers), else u = x; with
  *   MOE_F_RESIDUAL out = u + MoE(u), else out = MoE(u).
  *   topk_ids, topk_w, expert_offsets, sorted_rows: optional outputs (NULL =
- *   kept in the workspace only). */
+ *   kept in the workspace only).
+ * One token at the tuned geometry (D 2048, F 768, E 128, k 8, 16-byte aligned
+ * weight bases and strides, x and out) runs as one launch of the decode-stack
+ * kernel (see moe_decode_stack: bit-reproducible, fixed-point sums, the same
+ * range limits, reported by moe_workspace_status). */
 moe_status moe_layer(const float* x, const float* gate, const float* bias,
                      const moe_experts* W /* host */, int64_t T, int32_t k, int32_t flags,
                      float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,

@@ -182,10 +182,13 @@ static moe_status layer_impl(const float* x, const float* gate, const float* bia
   float* wts = topk_w ? topk_w : w.w;
   int32_t* offs = expert_offsets ? expert_offsets : w.offsets;
   int32_t* rows = sorted_rows ? sorted_rows : w.rows;
-  if (decode_fused_supported(dev, T, k, x)) {
+  if (T == 1 && decode_stack_layer_ok(dev, k) && decode_stack_io_ok(x, out)) {
+    // one token: the decode stack kernel with one layer
     trace("layer fused decode", T, D, F, E, k, W->format);
-    HIP_TRY(launch_decode_fused(x, gate, bias, dev, out, topk_ids, topk_w, expert_offsets,
-                                sorted_rows, flags, w, s));
+    const StackLayer sl{gate, bias, dev};
+    HIP_TRY(launch_decode_stack(x, 1, &sl, dev.fmt, (flags & MOE_F_PRENORM) != 0,
+                                (flags & MOE_F_RESIDUAL) != 0, out, topk_ids, topk_w,
+                                expert_offsets, sorted_rows, w, s));
     return MOE_OK;
   }
   auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
@@ -452,12 +455,11 @@ moe_status moe_decode_stack(const float* x, int32_t num_layers, const moe_stack_
   hipStream_t s = (hipStream_t)stream;
   const Workspace w = carve_workspace(ws, 1, D, F, E, k, MOE_F_PRENORM | MOE_F_RESIDUAL);
 
-  bool fused = aligned(x, 16) && aligned(outs, 16);
+  bool fused = decode_stack_io_ok(x, outs);
   for (int l = 0; l < num_layers && fused; ++l) {
     const ExpertsDev dv = to_dev(layers[l].experts);
-    fused = decode_fused_supported(dv, 1, k, x) && dv.fmt == W0->format;
+    fused = decode_stack_layer_ok(dv, k) && dv.fmt == W0->format;
   }
-  fused = fused && decode_stack_supported(W0->format);
   const int LM = decode_stack_max_layers();
   if (fused) {
     trace("decode stack fused", 1, D, F, E, k, W0->format);
@@ -468,9 +470,10 @@ moe_status moe_decode_stack(const float* x, int32_t num_layers, const moe_stack_
         sl[i] = StackLayer{layers[c + i].gate, layers[c + i].bias, to_dev(layers[c + i].experts)};
       const float* in = c == 0 ? x : outs + (size_t)(c - 1) * D;
       const bool pre = c > 0 || (flags & MOE_F_PRENORM);
-      HIP_TRY(launch_decode_stack(in, n, sl, W0->format, pre, outs + (size_t)c * D,
+      HIP_TRY(launch_decode_stack(in, n, sl, W0->format, pre, true, outs + (size_t)c * D,
                                   topk_ids ? topk_ids + (size_t)c * k : nullptr,
-                                  topk_w ? topk_w + (size_t)c * k : nullptr, w, s));
+                                  topk_w ? topk_w + (size_t)c * k : nullptr, nullptr, nullptr,
+                                  w, s));
     }
     return MOE_OK;
   }

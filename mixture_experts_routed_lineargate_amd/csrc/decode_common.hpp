@@ -1,12 +1,12 @@
-// Pieces shared by the single-token decode kernels (one layer per launch, and
-// a stack of layers per launch) for the Qwen3-MoE geometry: d_model 2048,
-// d_ff 768, 128 experts, top-8 (evidence page, Model card).
+// Pieces of the single-token decode kernel (one or more layers per launch) for
+// the Qwen3-MoE geometry: d_model 2048, d_ff 768, 128 experts, top-8 (evidence
+// page, Model card); the exchange and block-dot helpers also serve the
+// attention-side primitives.
 //
-// Both kernels run 256 workgroups of 512 threads, one per CU, all resident at
-// once.  Workgroup w serves expert slot j = w / 32 and part r = w % 32 of that
-// expert: gate/up rows f = 24r..24r+23 and down rows d = 64r..64r+63.  The first
-// 64 workgroups also form an 8 x 8 router grid over (16 experts, 256 rows of the
-// 2048 x 128 gate).
+// The decode kernel runs 256 workgroups of 512 threads, one per CU, all
+// resident at once.  Workgroup w serves expert slot j = w / 32 and part
+// r = w % 32 of that expert: gate/up rows f = 24r..24r+23 and down rows
+// d = 64r..64r+63.
 //
 // Exchange between workgroups: every published value is a 64-bit word
 // (tag << 32 | fp32 bits) written with an agent-scope store and read with
@@ -40,19 +40,9 @@ constexpr int NWAVE = NT / WAVE;     // 8
 constexpr int PARTS = NWG / K;       // workgroups per expert slot (32)
 constexpr int FPW = F / PARTS;       // gate/up rows per workgroup (24)
 constexpr int DPW = D / PARTS;       // down rows per workgroup (64)
-constexpr int OPW = D / NWG;         // outputs finished per workgroup (8)
-constexpr int REG = 8, RDS = 8;      // router grid: expert groups x row slices
-constexpr int RW = REG * RDS;        // router workgroups (64)
-constexpr int REPG = E / REG;        // experts per router workgroup (16)
-constexpr int RGRP = NT / REPG;      // row groups per router workgroup (32)
-constexpr int SLICE = D / RDS;       // gate rows per router row slice (256)
-constexpr int RROWS = SLICE / RGRP;  // gate rows per thread (8)
-constexpr int PREP = 32;             // replicas of the partial logits
 constexpr int HREP = 4;              // replicas of h
 static_assert(FPW * PARTS == F && DPW * PARTS == D, "split");
 static_assert(D / QK == WAVE, "one block per lane for gate/up rows");
-static_assert(D % RW == 0 && D / RW <= NT, "router workgroups initialise D / RW outputs each");
-static_assert(PREP * REPG == NT, "one replica store per thread");
 static_assert(E == 2 * WAVE, "two logits per lane");
 // Published values are replicated so that no cache line is polled by more than
 // 8 workgroups: coherent reads of one line from hundreds of CUs serialise.

@@ -95,6 +95,8 @@ struct StackArgs {
   float* outs;           // [L][D] o_l
   int32_t* ids;          // [L][K] or null
   float* w;              // [L][K] or null
+  int32_t* offsets;      // [E+1] or null: the grouping of the last layer's token (one layer)
+  int32_t* rows;         // [K] or null
   uint64_t* xa;          // [AREP][D] o replicas
   uint64_t* xz;          // [ZREP][ZC][E] replicas of the z copies
   uint64_t* xc;          // [HREP][K][F] h
@@ -104,6 +106,7 @@ struct StackArgs {
   uint32_t* err;         // bit 0: a poll timed out; bit 1: a value outside the fixed-point range
   int L;
   int prenorm0;
+  int residual;          // o_l includes in_l (always in a stack; a single layer may drop it)
   LayerPtrs layer[LMAX];
 };
 
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
     const int e_j = min(max(sel_e[slot], 0), E - 1);
     const float w_j = sel_w[slot];
     // in_l over this part's rows: slot 0 adds it to o_l
-    const float in_row = (slot == 0 && tid < DPW) ? xs[dr0 + tid] * inv : 0.f;
+    const float in_row = (slot == 0 && p.residual && tid < DPW) ? xs[dr0 + tid] * inv : 0.f;
     // ---- W + H: stream the weight share two groups ahead of the gate/up dots ----
     // A CU cannot have its whole ~153 KB share in flight: issuing it all at
     // once stalls every wavefront at the issue until most of it has arrived,
@@ -419,6 +422,16 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
       if (p.ids) p.ids[l * K + tid] = sel_e[tid];
       if (p.w) p.w[l * K + tid] = sel_w[tid];
     }
+    if (wg == 0 && l + 1 == L) {
+      // the grouping of one token: ids ascend, so slot j is flat row j
+      if (p.rows && tid < K) p.rows[tid] = tid;
+      if (p.offsets && tid <= E) {
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < K; ++j) c += sel_e[j] < tid;
+        p.offsets[tid] = c;
+      }
+    }
     // every wavefront leaves the layer together: measured faster than letting
     // the early ones start polling while the others still publish
     __syncthreads();
@@ -460,29 +473,44 @@ static bool stack_fits(int dev) {
 
 int decode_stack_max_layers() { return dec::LMAX; }
 
-bool decode_stack_supported(int fmt) {
+bool decode_stack_layer_ok(const ExpertsDev& W, int k) {
+  if (k != dec::K || W.D != dec::D || W.F != dec::F || W.E != dec::E) return false;
+  if (W.fmt != MOE_FMT_Q8_0 && W.fmt != MOE_FMT_Q4) return false;
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  // weight rows are read as 16-byte pieces
+  if (!a16(W.gate) || !a16(W.up) || !a16(W.down) || (W.gate_stride & 15) ||
+      (W.up_stride & 15) || (W.down_stride & 15))
+    return false;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
-  return fmt == MOE_FMT_Q8_0 ? dec::stack_fits<MOE_FMT_Q8_0>(dev) : dec::stack_fits<MOE_FMT_Q4>(dev);
+  return W.fmt == MOE_FMT_Q8_0 ? dec::stack_fits<MOE_FMT_Q8_0>(dev) : dec::stack_fits<MOE_FMT_Q4>(dev);
+}
+
+bool decode_stack_io_ok(const float* x, const float* out) {
+  return ((uintptr_t)x & 15) == 0 && ((uintptr_t)out & 15) == 0;
 }
 
 hipError_t launch_decode_stack(const float* x, int L, const StackLayer* layers, int fmt,
-                               bool prenorm0, float* outs, int32_t* ids, float* w,
-                               const Workspace& ws, hipStream_t s) {
+                               bool prenorm0, bool residual, float* outs, int32_t* ids, float* w,
+                               int32_t* offsets, int32_t* rows, const Workspace& ws,
+                               hipStream_t s) {
   if (L <= 0 || L > dec::LMAX) return hipErrorInvalidValue;
   dec::StackArgs a{};
   a.x = x;
   a.outs = outs;
   a.ids = ids;
   a.w = w;
+  a.offsets = offsets;
+  a.rows = rows;
+  a.residual = residual ? 1 : 0;
   char* sync = (char*)ws.sync;
   a.err = ws.sync + ERR_WORD_OFF / sizeof(uint32_t);
-  a.epochs = (uint32_t*)(sync + 4096);                    // [256] u32, shared with the layer kernel
+  a.epochs = (uint32_t*)(sync + 4096);                    // [256] u32
   a.xz = (uint64_t*)(sync + 65536);                       // [32][8][128] u64 (256 KiB)
   a.xc = (uint64_t*)(sync + 327680);                      // [4][8][768] u64 (192 KiB)
   a.xa = (uint64_t*)(sync + 524288);                      // [32][2048] u64 (512 KiB)
-  // the accumulators sit where no other kernel writes (the layer kernel ends at
-  // 640 KiB, the small-batch routing starts at ROUTE_SYNC_OFF)
+  // the accumulators sit where no other kernel writes (the small-batch routing
+  // starts at ROUTE_SYNC_OFF)
   a.oacc = (uint64_t*)(sync + STACK_ACC_OFF);                     // [24][2048] u64 (384 KiB)
   a.zacc = (uint64_t*)(sync + STACK_ACC_OFF + 393216);            // [24][8][128] u64 (192 KiB)
   static_assert(524288 + 524288 <= STACK_ACC_OFF &&

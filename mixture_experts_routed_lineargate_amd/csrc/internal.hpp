@@ -188,24 +188,22 @@ hipError_t launch_skinny_down(const _Float16* hhi, const _Float16* hlo, int a_mo
                               const ExpertsDev& W, const int32_t* offsets, const int32_t* rows,
                               int64_t R, int k, float* y, bool split, hipStream_t s);
 
-// fused single-token decode layer (D 2048, F 768, E 128, k 8)
-bool decode_fused_supported(const ExpertsDev& W, int64_t T, int k, const float* x);
-hipError_t launch_decode_fused(const float* x, const float* gate, const float* bias,
-                               const ExpertsDev& W, float* out, int32_t* ids, float* w,
-                               int32_t* offsets, int32_t* rows, int flags, const Workspace& ws,
-                               hipStream_t s);
-
-// single-token decode through a stack of layers in one launch (same geometry)
+// single-token decode through one layer or a stack of layers in one launch
+// (D 2048, F 768, E 128, k 8)
 struct StackLayer {
   const float* gate;
   const float* bias;
   ExpertsDev W;
 };
 int decode_stack_max_layers();
-bool decode_stack_supported(int fmt);
+// one layer's pointers and the token's fit the fused kernel (geometry, alignment,
+// all workgroups resident)
+bool decode_stack_layer_ok(const ExpertsDev& W, int k);
+bool decode_stack_io_ok(const float* x, const float* out);
 hipError_t launch_decode_stack(const float* x, int L, const StackLayer* layers, int fmt,
-                               bool prenorm0, float* outs, int32_t* ids, float* w,
-                               const Workspace& ws, hipStream_t s);
+                               bool prenorm0, bool residual, float* outs, int32_t* ids, float* w,
+                               int32_t* offsets, int32_t* rows, const Workspace& ws,
+                               hipStream_t s);
 
 // attention-side primitives (attn_prep.hip); ws: 256 header bytes (error word at 64),
 // [T][N] tagged 64-bit published rows, then (at attn_count_offset) [ceil(T/8)][Hq + Hkv]

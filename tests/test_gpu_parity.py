@@ -518,8 +518,12 @@ def scaled_down_arena(arena, D, F, fmt):
     (9, 160, 96, 40, 5, 1),         # generic kernels
 ])
 def test_down_scale_linearity(T, D, F, E, k, fmt):
-    """Doubling every W_down scale doubles the output bit for bit (no residual,
-    MOE_F_DETERMINISTIC): the scale enters every kernel as an exact factor."""
+    """Doubling every W_down scale doubles the output (no residual,
+    MOE_F_DETERMINISTIC): the scale enters every kernel as an exact factor, so the
+    grouped and generic paths double bit for bit.  The single-token kernel sums
+    the slots' outputs in fixed point with an absolute step of 2^-24, so there
+    each of the 8 terms may round differently: |out2 - 2 out1| <= 8 * 2^-24, plus
+    one fp32 rounding of the sum."""
     c = cases.router_case(f"lin{T}", 700 + T, T, D, F, E, k, fmt, True, DEV,
                           host_experts=(D != 2048))
     c2 = cases.Case(c.name, T, D, F, E, k, fmt, x=c.x, G=c.G, b=c.b,
@@ -527,7 +531,12 @@ def test_down_scale_linearity(T, D, F, E, k, fmt):
     g1 = run_layer(c, M.F_DETERMINISTIC)
     g2 = run_layer(c2, M.F_DETERMINISTIC)
     assert np.array_equal(g1["ids"], g2["ids"])
-    assert np.array_equal(g2["out"].view(np.uint32), (2 * g1["out"]).view(np.uint32))
+    if T == 1 and D == 2048:
+        diff = np.abs(g2["out"].astype(np.float64) - 2.0 * g1["out"].astype(np.float64))
+        bound = 8 * 2.0 ** -24 + 2.0 ** -23 * np.abs(g2["out"].astype(np.float64))
+        assert (diff <= bound).all(), f"worst {np.max(diff - bound):.3e} beyond the fixed-point bound"
+    else:
+        assert np.array_equal(g2["out"].view(np.uint32), (2 * g1["out"]).view(np.uint32))
     r = O.moe_layer(c.x, c.G, c.b, c.oracle_experts(), k)
     check_out(g1["out"], r["out"], "linearity base layer")
 
