@@ -40,12 +40,10 @@ constexpr int NWAVE = NT / WAVE;     // 8
 constexpr int PARTS = NWG / K;       // workgroups per expert slot (32)
 constexpr int FPW = F / PARTS;       // gate/up rows per workgroup (24)
 constexpr int DPW = D / PARTS;       // down rows per workgroup (64)
-constexpr int HREP = 4;              // replicas of h
+constexpr int HREP = 2;              // replicas of h
 static_assert(FPW * PARTS == F && DPW * PARTS == D, "split");
 static_assert(D / QK == WAVE, "one block per lane for gate/up rows");
 static_assert(E == 2 * WAVE, "two logits per lane");
-// Published values are replicated so that no cache line is polled by more than
-// 8 workgroups: coherent reads of one line from hundreds of CUs serialise.
 
 template <int FMT>
 struct Geo {

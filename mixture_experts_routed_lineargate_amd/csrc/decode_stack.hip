@@ -43,8 +43,8 @@
 // launch reaches every later output.  Wavefront 0 adds the o rows and
 // wavefronts 1 and 2 the z share, so the two kinds of adds are in flight
 // together.  The add that brings the count to its total returns the whole sum:
-// that lane decodes it and publishes it (o_l(d) into 32 replicas and into outs,
-// a z copy into 32 replicas) as tagged words; the reader sums the 8 z copies
+// that lane decodes it and publishes it (o_l(d) into 8 replicas and into outs,
+// a z copy into 8 replicas) as tagged words; the reader sums the 8 z copies
 // in copy order.  A contribution to o must stay below 2^27 in magnitude and a
 // workgroup's z share below 2^22, so that the sums fit their fields; beyond
 // that it counts as invalid and sets bit 1 of the workspace's error word.
@@ -53,17 +53,21 @@
 // last layer's S step), except the last layer's o words, which the lane
 // completing each one zeroes.
 //
-// Replicated words: published values are copied so that no cache line is
-// polled by more than 8 workgroups (coherent reads of one line from hundreds
-// of CUs serialise).  Tags are the launch counter + layer + 1, as for h.
+// Replicated words: coherent reads of one cache line from hundreds of CUs
+// queue behind each other, so published values are copied: o and the z copies
+// 8 times (32 pollers per line), h twice (16 pollers per line).  With 1, 2, 4,
+// 8, 16 and 32 copies of o and z the layer took 14.58, 14.37, 14.32, 14.31,
+// 14.42 and 14.53 us, with 1, 2 and 4 copies of h 14.38, 14.25 and 14.31 us:
+// fewer copies mean fewer stores before a value is out, more mean shorter
+// poll queues.  Tags are the launch counter + layer + 1.
 #include "decode_common.hpp"
 
 namespace moe {
 namespace dec {
 
 constexpr int LMAX = 24;        // layers per launch (per-layer pointers ride in the kernel arguments)
-constexpr int AREP = 32;        // replicas of o
-constexpr int ZREP = 32;        // replicas of the z copies
+constexpr int AREP = 8;         // replicas of o
+constexpr int ZREP = 8;         // replicas of the z copies
 constexpr int ZC = 8;           // partial copies of z
 // Low fields of an accumulator word: a count of contributions (4 bits for o's
 // 8, 6 for a z copy's 32) and above it a count of invalid ones; the
@@ -506,9 +510,12 @@ hipError_t launch_decode_stack(const float* x, int L, const StackLayer* layers, 
   char* sync = (char*)ws.sync;
   a.err = ws.sync + ERR_WORD_OFF / sizeof(uint32_t);
   a.epochs = (uint32_t*)(sync + 4096);                    // [256] u32
-  a.xz = (uint64_t*)(sync + 65536);                       // [32][8][128] u64 (256 KiB)
-  a.xc = (uint64_t*)(sync + 327680);                      // [4][8][768] u64 (192 KiB)
-  a.xa = (uint64_t*)(sync + 524288);                      // [32][2048] u64 (512 KiB)
+  a.xz = (uint64_t*)(sync + 65536);                       // [ZREP][8][128] u64 (64 KiB)
+  a.xc = (uint64_t*)(sync + 327680);                      // [HREP][8][768] u64 (96 KiB)
+  a.xa = (uint64_t*)(sync + 524288);                      // [AREP][2048] u64 (128 KiB)
+  static_assert(65536 + dec::ZREP * dec::ZC * dec::E * 8 <= 327680 &&
+                327680 + dec::HREP * dec::K * dec::F * 8 <= 524288 &&
+                524288 + dec::AREP * dec::D * 8 <= STACK_ACC_OFF, "exchange regions");
   // the accumulators sit where no other kernel writes (the small-batch routing
   // starts at ROUTE_SYNC_OFF)
   a.oacc = (uint64_t*)(sync + STACK_ACC_OFF);                     // [24][2048] u64 (384 KiB)
