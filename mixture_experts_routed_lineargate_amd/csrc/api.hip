@@ -524,7 +524,7 @@ moe_status moe_attn_prep(const float* x, int64_t T, const moe_attn_weights* W, c
   const int D = W->d_model, Hq = W->n_q_heads, Hkv = W->n_kv_heads, hd = W->head_dim;
   if (T < 0 || D <= 0 || D % QK || Hq <= 0 || Hkv <= 0 || hd <= 0 || hd % 16 || max_pos < 0)
     return MOE_E_SHAPE;
-  if (D > 3584 || hd > 256 || Hq > 1024 || Hkv > 1024) return MOE_E_UNSUPPORTED;   // LDS <= 64 KB
+  if (D > 3584 || hd > 256 || Hq > 1024 || Hkv > 1024) return MOE_E_UNSUPPORTED;   // LDS <= 90 KB
   if (!(rope_theta > 1.0f) || !(eps >= 0.0f)) return MOE_E_SHAPE;
   if (T == 0) return MOE_OK;
   if (!x || !pos || !q || !W->w_qkv || !W->attn_gain || !W->q_gain || !W->k_gain) return MOE_E_NULLPTR;

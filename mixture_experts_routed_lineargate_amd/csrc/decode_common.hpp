@@ -304,28 +304,17 @@ __device__ inline float block_dot_dig(const uint8_t* lds, uint32_t blk_off, cons
   return half_bits_to_float((uint16_t)sbits) * d.s * r;
 }
 
-// Digit planes of nblk activation blocks of v*scale, built cooperatively from
-// LDS: thread t of the first nblk*32/EPT threads takes EPT consecutive elements
-// (block t*EPT/32; the 32/EPT threads of a block are adjacent lanes, reduced
-// with DPP).  Writes dig[blk][3 planes][8 dwords] (bytes) and
-// scl[blk] = (s, sx) to LDS; the caller places a barrier after.  Every thread
-// of the workgroup must call it (the DPP reductions need whole wavefronts).
+// Digit planes from registers: piece t (elements EPT*t .. EPT*t + EPT-1, block
+// t*EPT/32) is held by a lane whose wavefront holds the block's other pieces on
+// the adjacent lanes (reduced with DPP); `on` is false for pieces past the
+// last block.  Writes dig[blk][3 planes][8 dwords] (bytes) and scl[blk] =
+// (s, sx) to LDS; the caller places a barrier after.  Every lane of the
+// wavefront must call it.
 template <int FMT, int EPT>
-__device__ inline void act_digits_lds(const float* v, float scale, int nblk, uint8_t* dig,
-                                      float2* scl) {
+__device__ inline void act_digits_reg(const float* x, bool on, int t, uint8_t* dig, float2* scl) {
   static_assert(EPT == 2 || EPT == 4, "8 or 16 threads per block");
   constexpr int TPB = QK / EPT;
-  const int t = threadIdx.x;
-  const bool on = t < TPB * nblk;
   const int blk = t / TPB, e0 = EPT * (t % TPB);
-  float x[EPT];
-  if constexpr (EPT == 4) {
-    const float4 q = on ? *(const float4*)(v + 4 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
-    x[0] = q.x * scale; x[1] = q.y * scale; x[2] = q.z * scale; x[3] = q.w * scale;
-  } else {
-    const float2 q = on ? *(const float2*)(v + 2 * t) : make_float2(0.f, 0.f);
-    x[0] = q.x * scale; x[1] = q.y * scale;
-  }
   float m = 0.f;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) m = fmaxf(m, fabsf(x[i]));
@@ -360,6 +349,26 @@ __device__ inline void act_digits_lds(const float* v, float scale, int nblk, uin
     base[2 * 32 + 4 * j + n] = (uint8_t)c;
   }
   if (t % TPB == 0) scl[blk] = make_float2(__builtin_amdgcn_ldexpf(1.0f, -sh), __int_as_float(sx));
+}
+
+// Digit planes of nblk activation blocks of v*scale, built cooperatively from
+// LDS: thread t of the first nblk*32/EPT threads takes EPT consecutive elements
+// (act_digits_reg's piece t).  Every thread of the workgroup must call it.
+template <int FMT, int EPT>
+__device__ inline void act_digits_lds(const float* v, float scale, int nblk, uint8_t* dig,
+                                      float2* scl) {
+  constexpr int TPB = QK / EPT;
+  const int t = threadIdx.x;
+  const bool on = t < TPB * nblk;
+  float x[EPT];
+  if constexpr (EPT == 4) {
+    const float4 q = on ? *(const float4*)(v + 4 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
+    x[0] = q.x * scale; x[1] = q.y * scale; x[2] = q.z * scale; x[3] = q.w * scale;
+  } else {
+    const float2 q = on ? *(const float2*)(v + 2 * t) : make_float2(0.f, 0.f);
+    x[0] = q.x * scale; x[1] = q.y * scale;
+  }
+  act_digits_reg<FMT, EPT>(x, on, t, dig, scl);
 }
 
 // Load block blk of act_digits_lds's output.
