@@ -8,8 +8,12 @@
 // 64-value chunks two deep) are few and latency-bound.  Here the weight slice
 // is the unit of work: a workgroup owns one active expert and a slice of its
 // weight rows (gate/up: 16 gate + 16 up rows = 16 columns of h; down: 64 rows),
-// loads the whole slice (K = 2048 or 768) into LDS at once, and applies it to
-// every row routed to that expert, 32 rows per pass.  The four wavefronts split
+// copies the whole slice (K = 2048 or 768) from global memory straight into LDS
+// at once (LDS DMA, no registers), and applies it to every row routed to that
+// expert, 32 rows per pass.  Activation fragments come through buffer loads; a
+// padding row of a pass (an expert with 7 rows fills 7 of the 16 rows of an
+// M-tile) gets an offset past the buffer's range, which returns zeros without
+// fetching.  The four wavefronts split
 // K into quarters and add their partial tiles in LDS in wavefront order, so the
 // result does not depend on timing.  Weight rows sit in LDS with a stride that
 // is an odd multiple of 16 bytes, which puts the 16 rows x 4 lane groups of a
@@ -43,8 +47,6 @@ struct Geo {
   static constexpr int NS = WR / 16;              // 16-row n-subtiles
   static constexpr int COLS = STAGE == STAGE_GATEUP ? 16 : 64; // output columns per workgroup
   static constexpr int NCB = N / COLS;            // workgroups per expert
-  static constexpr int CHUNKS = WR * RB / 16;     // 16-byte pieces of the slice
-  static constexpr int LPT = (CHUNKS + NT - 1) / NT;   // pieces per thread
   static constexpr int BPW = K / QK / NW;         // blocks per wavefront
   static constexpr int W_BYTES = WR * RBP;
   static constexpr int RED_BYTES = (NW - 1) * 2 * NS * WAVE * 16;
@@ -74,22 +76,31 @@ struct Args {
 // wavefront's quarter of K: the wavefront's partial tile goes to acc.
 template <int FMT, int STAGE, bool SPLIT, int MT>
 __device__ inline void pass_tiles(const Args& p, const uint8_t* wl, const int* m_src, int kb0,
-                                  int lane, f32x4 (&acc)[2][Geo<FMT, STAGE>::NS]) {
+                                  int lane, int nv, f32x4 (&acc)[2][Geo<FMT, STAGE>::NS]) {
   using G = Geo<FMT, STAGE>;
   constexpr int PL = SPLIT ? 2 : 1;
   constexpr int PDM = MT == 1 ? 2 * PD : PD;        // deeper prefetch when one M-tile
   const int ln = lane % 16, lg = lane / 16;
-  int64_t arow[MT];
+  // activation rows through buffer loads: a padding row's lanes get an offset past
+  // the buffer's range, so the load returns zeros without fetching anything
+  constexpr int NREC = 1 << 30;                     // > any activation plane (512 rows x K x 2 bytes)
+  const __amdgpu_buffer_rsrc_t rs[2] = {
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.ahi, 0, NREC, 0x00020000),
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.alo, 0, NREC, 0x00020000)};
+  int voff[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) arow[m] = (int64_t)m_src[16 * m + ln] * G::K;
+  for (int m = 0; m < MT; ++m)
+    voff[m] = 16 * m + ln < nv ? m_src[16 * m + ln] * G::K * 2 : NREC;
   h8 ra[PDM][MT][PL];                               // prefetch ring of activation fragments
   auto aload = [&](int j, int slot) {
-    const int o = (kb0 + j) * QK + 8 * lg;
+    const int o = ((kb0 + j) * QK + 8 * lg) * 2;
 #pragma unroll
     for (int pl = 0; pl < PL; ++pl) {
-      const _Float16* a = pl ? p.alo : p.ahi;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) ra[slot][m][pl] = *(const h8*)(a + arow[m] + o);
+      for (int m = 0; m < MT; ++m) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs[pl], voff[m] + o, 0, 0);
+        ra[slot][m][pl] = __builtin_bit_cast(h8, v);
+      }
     }
   };
 #pragma unroll
@@ -180,28 +191,21 @@ __global__ __launch_bounds__(NT, 2) void skinny_kernel(Args p) {
     const int u = it / G::NCB, cb = it % G::NCB;
     const int e = act[u], r0 = aoff[2 * u], r1 = aoff[2 * u + 1], re = r1 - r0;
 
-    // ---- the weight slice, all of it in flight at once ----
+    // ---- the weight slice, all of it in flight at once, straight into LDS: wavefront
+    // w copies rows w, w + 4, ... (a row's RB/16 pieces in 64-lane instructions, so
+    // the padded row stride is kept) ----
     const int n0 = cb * (STAGE == STAGE_GATEUP ? 16 : G::COLS);
-    u32x4 wv[G::LPT];
-#pragma unroll
-    for (int i = 0; i < G::LPT; ++i) {
-      const int c = min(i * NT + tid, G::CHUNKS - 1);   // clamped: unconditional loads
-      const int row = c / (G::RB / 16), col = c % (G::RB / 16);
+    const int es = __builtin_amdgcn_readfirstlane(e), ns = __builtin_amdgcn_readfirstlane(n0);
+    for (int row = __builtin_amdgcn_readfirstlane(wave); row < G::WR; row += NW) {
       const uint8_t* src;
       if constexpr (STAGE == STAGE_GATEUP)
-        src = row < 16 ? p.w0 + (int64_t)e * p.s0 + (int64_t)(n0 + row) * G::RB
-                       : p.w1 + (int64_t)e * p.s1 + (int64_t)(n0 + row - 16) * G::RB;
+        src = row < 16 ? p.w0 + (int64_t)es * p.s0 + (int64_t)(ns + row) * G::RB
+                       : p.w1 + (int64_t)es * p.s1 + (int64_t)(ns + row - 16) * G::RB;
       else
-        src = p.w0 + (int64_t)e * p.s0 + (int64_t)(n0 + row) * G::RB;
-      wv[i] = __builtin_nontemporal_load((const u32x4*)(src + 16 * col));
-    }
+        src = p.w0 + (int64_t)es * p.s0 + (int64_t)(ns + row) * G::RB;
 #pragma unroll
-    for (int i = 0; i < G::LPT; ++i) {
-      const int c = i * NT + tid;
-      if (c < G::CHUNKS) {
-        const int row = c / (G::RB / 16), col = c % (G::RB / 16);
-        *(u32x4*)(wl + row * G::RBP + 16 * col) = wv[i];
-      }
+      for (int c0 = 0; c0 < G::RB / 16; c0 += WAVE)
+        if (c0 + lane < G::RB / 16) gg::lds_dma16(src, 16u * (c0 + lane), wl + row * G::RBP + 16 * c0);
     }
 
     for (int pass = 0; pass * MROWS < re; ++pass) {
@@ -218,13 +222,15 @@ __global__ __launch_bounds__(NT, 2) void skinny_kernel(Args p) {
         m_src[tid] = src;
         m_flat[tid] = fl;
       }
+      if (pass == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's slice rows
       __syncthreads();                                // weights (first pass) and row metadata
       f32x4 acc[2][G::NS];
-      if (re - pass * MROWS <= 16)
-        pass_tiles<FMT, STAGE, SPLIT, 1>(p, wl, m_src, kb0, lane, acc);
+      const int nv = min(re - pass * MROWS, MROWS);
+      if (nv <= 16)
+        pass_tiles<FMT, STAGE, SPLIT, 1>(p, wl, m_src, kb0, lane, nv, acc);
       else
-        pass_tiles<FMT, STAGE, SPLIT, 2>(p, wl, m_src, kb0, lane, acc);
-      const int mt = re - pass * MROWS <= 16 ? 1 : 2;
+        pass_tiles<FMT, STAGE, SPLIT, 2>(p, wl, m_src, kb0, lane, nv, acc);
+      const int mt = nv <= 16 ? 1 : 2;
 
       // ---- K quarters summed in wavefront order, epilogue by wavefront 0 ----
       f32x4* rd = (f32x4*)red;
