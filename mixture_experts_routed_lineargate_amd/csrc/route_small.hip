@@ -71,7 +71,6 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
   __shared__ __attribute__((aligned(16))) float xs[TPG][SL + 4];    // rows 16-byte aligned
   __shared__ float gs[SL][EMAX];
   __shared__ float pl[NS_MAX * (EMAX + 1)];
-  __shared__ float sums[EMAX + 1];
   __shared__ __attribute__((aligned(16))) float lgt[EMAX];
   __shared__ int top[KMAX];
   __shared__ int sids[KMAX];
@@ -168,35 +167,56 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
     for (int i = 0; i < QW; ++i)
       if (i * NT + tid < nw) pl[i * NT + tid] = vals[i];
     __syncthreads();
-    if (tid <= E) {
-      float a = 0.f;
+    // logits: thread e < E sums its expert's partials in slice order, and (every
+    // one of them, the same sums in the same order) the sums of squares for inv;
+    // the slots past E hold NaN, which no comparison counts
+    float ssq = 0.f;
 #pragma unroll 8
-      for (int q = 0; q < ns; ++q) a += pl[q * (E + 1) + tid];   // slice order
-      sums[tid] = a;
-    }
-    __syncthreads();
-    const float inv = p.prenorm ? 1.0f / sqrtf(sums[E] / (float)D + PRENORM_EPS) : 1.0f;
-    // the top-k by rank counting over the workgroup (four threads a logit; k
-    // rounds of a wave arg-max on one wavefront took ~0.5 us longer): another logit
-    // outranks e if it is larger, or equal with a lower index, so expert e is
-    // selected iff fewer than k logits outrank it.  Slots start at their own
-    // index, so the ids are in [0, E) whatever the logits hold.
-    if (wave == 0) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ee = i * WAVE + lane;
-        float l = 0.f;
-        if (ee < E) {
-          l = sums[ee] * inv;
-          if (p.bias) l += bv[i];
-        }
-        lgt[ee] = l;
+    for (int q = 0; q < ns; ++q) ssq += pl[q * (E + 1) + E];
+    const float inv = p.prenorm ? 1.0f / sqrtf(ssq / (float)D + PRENORM_EPS) : 1.0f;
+    if (tid < EMAX) {
+      float l = __builtin_nanf("");
+      if (tid < E) {
+        float a = 0.f;
+#pragma unroll 8
+        for (int q = 0; q < ns; ++q) a += pl[q * (E + 1) + tid];   // slice order
+        l = p.bias ? fmaf(a, inv, bv[wave]) : a * inv;   // bias of expert wave * WAVE + lane
       }
-      if (lane < KMAX) top[lane] = lane;
-      if (p.inv && lane == 0) p.inv[b] = inv;
+      lgt[tid] = l;
+    }
+    if (tid < KMAX) top[tid] = -1;
+    if (p.inv && tid == 0) p.inv[b] = inv;
+    __syncthreads();
+    // the top-k by rank counting over the workgroup, four threads a logit: another
+    // logit outranks e if it is larger, or equal with a lower index, so expert e is
+    // selected iff fewer than k logits outrank it.  A first pass counts only the
+    // logits >= lgt[e] (one compare a pair); less one (e itself) that is e's rank
+    // whenever no other logit equals it.  m >= 2 equal logits under c larger ones
+    // all claim slot c + m - 1 and leave slot c empty, so when the k slots are all
+    // filled no tie reaches the top k and the slots hold the exact ranks.
+    // Otherwise a second pass ranks with the full comparison, every slot preset to
+    // its own index, so the ids are in [0, E) whatever the logits hold.
+    {
+      const int e = tid >> 2, q = tid & 3;
+      const float le = lgt[e];
+      float4 v[EMAX / 16];
+#pragma unroll
+      for (int i = 0; i < EMAX / 16; ++i) v[i] = *(const float4*)(lgt + (EMAX / 4) * q + 4 * i);
+      int ge = 0;
+#pragma unroll
+      for (int i = 0; i < EMAX / 16; ++i)
+        ge += (v[i].x >= le) + (v[i].y >= le) + (v[i].z >= le) + (v[i].w >= le);
+      ge += dpp<DPP_QUAD_1032>(ge);
+      ge += dpp<DPP_QUAD_2301>(ge);
+      if (q == 0 && e < E && ge >= 1 && ge <= k) top[ge - 1] = e;
     }
     __syncthreads();
-    {
+    int hole = 0;
+    for (int r = 0; r < k; ++r) hole |= top[r] < 0;
+    if (hole) {                                       // uniform: every thread read the same slots
+      __syncthreads();
+      if (tid < KMAX) top[tid] = tid;
+      __syncthreads();
       const int e = tid >> 2, q = tid & 3;
       int cnt = 0;
       if (e < E) {
@@ -211,23 +231,27 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
       cnt += dpp<DPP_QUAD_1032>(cnt);
       cnt += dpp<DPP_QUAD_2301>(cnt);
       if (q == 0 && e < E && cnt < k) top[cnt] = e;
+      __syncthreads();
     }
-    __syncthreads();
-    if (wave == 0 && lane < k) {
-      // renormalised softmax over the winners, summed in rank order; outputs in
-      // ascending id
+    if (wave == 0) {
+      // renormalised softmax over the winners: lane r < k takes winner r (rank
+      // order); the denominator is summed in rank order; outputs in ascending id
+      const int me = min(max(top[min(lane, k - 1)], 0), E - 1);
       const float lmax = lgt[min(max(top[0], 0), E - 1)];
+      const float ex = expf(lgt[me] - lmax);
       float den = 0.f;
-      for (int r = 0; r < k; ++r) den += expf(lgt[min(max(top[r], 0), E - 1)] - lmax);
-      const int me = min(max(top[lane], 0), E - 1);
+      for (int r = 0; r < k; ++r) den += __shfl(ex, r, WAVE);
       int rank = 0;
       for (int r = 0; r < k; ++r) rank += top[r] < me;
       rank = min(rank, k - 1);
-      p.ids[b * k + rank] = me;
-      sids[rank] = me;
-      p.w[b * k + rank] = expf(lgt[me] - lmax) / den;
+      if (lane < k) {
+        p.ids[b * k + rank] = me;
+        sids[rank] = me;
+        p.w[b * k + rank] = ex / den;
+      }
     }
-    // input planes of token b
+    // input planes of token b (element by element: a packed conversion would round
+    // ties unlike the other kernels that write planes)
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
       const int d = 4 * (j * NT + tid);
