@@ -6,20 +6,28 @@
 //
 // With so few rows the grouped GEMM's tiles (256 weight rows, a K loop of
 // 64-value chunks two deep) are few and latency-bound.  Here the weight slice
-// is the unit of work: a workgroup owns one active expert and a slice of its
-// weight rows (gate/up: 16 gate + 16 up rows = 16 columns of h; down: 64 rows),
-// copies the whole slice (K = 2048 or 768) from global memory straight into LDS
-// at once (LDS DMA, no registers), and applies it to every row routed to that
-// expert, 32 rows per pass.  Activation fragments come through buffer loads; a
-// padding row of a pass (an expert with 7 rows fills 7 of the 16 rows of an
-// M-tile) gets an offset past the buffer's range, which returns zeros without
-// fetching.  The four wavefronts split
-// K into quarters and add their partial tiles in LDS in wavefront order, so the
-// result does not depend on timing.  Weight rows sit in LDS with a stride that
-// is an odd multiple of 16 bytes, which puts the 16 rows x 4 lane groups of a
-// fragment read in distinct banks.  The grid is persistent: every workgroup
-// compacts the list of experts with rows from expert_offsets (in LDS) and walks
-// the (active expert, slice) items with a stride of the grid size.
+// is the unit of work: an item is one 16-row unit of an active expert's routed
+// rows (an expert with 7 rows is one unit, one with 17-32 rows two) and a slice
+// of the expert's weight rows (gate/up: 16 gate + 16 up rows = 16 columns of h;
+// down: 64 rows).  The workgroup copies the whole slice (K = 2048 or 768) from
+// global memory straight into LDS at once (LDS DMA, no registers) and applies
+// it to the unit's rows, one M-tile.  Activation fragments come through buffer
+// loads; a padding row of the M-tile (7 rows fill 7 of its 16) gets an offset
+// past the buffer's range, which returns zeros without fetching.  The four
+// wavefronts split K into quarters and add their partial tiles in LDS in
+// wavefront order, so the result does not depend on timing.  Weight rows sit in
+// LDS with a stride that is an odd multiple of 16 bytes, which puts the 16 rows
+// x 4 lane groups of a fragment read in distinct banks.  The grid is
+// persistent: every workgroup builds the list of units from expert_offsets (in
+// LDS) and walks the (unit, slice) items with a stride of the grid size.
+//
+// Why units of one M-tile: a hot expert's 17-32 rows as one two-tile item took
+// well over twice a one-tile item (the prefetch ring is half as deep per tile),
+// two such items on one CU set the end of the launch, and the two-tile code
+// kept the kernel at two workgroups per CU.  With one tile the 4-bit kernels fit
+// three workgroups per CU (registers and LDS), and each CU keeps three items'
+// slice copies and dots in flight; the units of a slice read the same weight
+// bytes, which the caches serve after the first.
 #include "mfma_frag.hpp"
 
 namespace moe {
@@ -28,10 +36,11 @@ namespace sk {
 using gg::h8;
 constexpr int NT = 256;       // 4 wavefronts
 constexpr int NW = NT / WAVE;
-constexpr int MROWS = 32;     // rows per pass (two 16-row M-tiles)
-constexpr int PD = 4;         // activation-fragment prefetch depth (blocks)
+constexpr int MROWS = 16;     // rows per item (one M-tile)
+constexpr int PD = 8;         // activation-fragment prefetch depth (blocks)
 constexpr int D_TUNED = 2048, F_TUNED = 768;
 constexpr int E_MAX = 256;    // experts per layer this kernel takes
+constexpr int U_MAX = E_MAX + 512 / 16;   // 16-row units: at most one per expert + one per 16 rows
 enum { STAGE_GATEUP = 0, STAGE_DOWN = 1 };
 
 __host__ __device__ constexpr int padded_row(int rb) { return ((rb / 16) % 2 == 0) ? rb + 16 : rb; }
@@ -49,10 +58,9 @@ struct Geo {
   static constexpr int NCB = N / COLS;            // workgroups per expert
   static constexpr int BPW = K / QK / NW;         // blocks per wavefront
   static constexpr int W_BYTES = WR * RBP;
-  static constexpr int RED_BYTES = (NW - 1) * 2 * NS * WAVE * 16;
+  static constexpr int RED_BYTES = (NW - 1) * NS * WAVE * 16;
   static_assert(RB % 16 == 0 && (RBP / 16) % 2 == 1, "row stride");
   static_assert(K % (QK * NW) == 0 && N % COLS == 0, "shape");
-  static_assert(BPW % PD == 0 || BPW >= PD, "prefetch ring");
 };
 
 struct Args {
@@ -72,14 +80,13 @@ struct Args {
   float* y;                   // down: y [R][N] in flat order
 };
 
-// One pass over up to 32 rows (MT 16-row M-tiles) of the current item, for this
-// wavefront's quarter of K: the wavefront's partial tile goes to acc.
-template <int FMT, int STAGE, bool SPLIT, int MT>
-__device__ inline void pass_tiles(const Args& p, const uint8_t* wl, const int* m_src, int kb0,
-                                  int lane, int nv, f32x4 (&acc)[2][Geo<FMT, STAGE>::NS]) {
+// The item's rows (nv <= 16 of them real, one M-tile) against this wavefront's
+// quarter of K: the wavefront's partial tile of every n-subtile goes to acc.
+template <int FMT, int STAGE, bool SPLIT>
+__device__ inline void pass_tile(const Args& p, const uint8_t* wl, const int* m_src, int kb0,
+                                 int lane, int nv, f32x4 (&acc)[Geo<FMT, STAGE>::NS]) {
   using G = Geo<FMT, STAGE>;
   constexpr int PL = SPLIT ? 2 : 1;
-  constexpr int PDM = MT == 1 ? 2 * PD : PD;        // deeper prefetch when one M-tile
   const int ln = lane % 16, lg = lane / 16;
   // activation rows through buffer loads: a padding row's lanes get an offset past
   // the buffer's range, so the load returns zeros without fetching anything
@@ -87,32 +94,22 @@ __device__ inline void pass_tiles(const Args& p, const uint8_t* wl, const int* m
   const __amdgpu_buffer_rsrc_t rs[2] = {
       __builtin_amdgcn_make_buffer_rsrc((void*)p.ahi, 0, NREC, 0x00020000),
       __builtin_amdgcn_make_buffer_rsrc((void*)p.alo, 0, NREC, 0x00020000)};
-  int voff[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-    voff[m] = 16 * m + ln < nv ? m_src[16 * m + ln] * G::K * 2 : NREC;
-  h8 ra[PDM][MT][PL];                               // prefetch ring of activation fragments
+  const int voff = ln < nv ? m_src[ln] * G::K * 2 : NREC;
+  h8 ra[PD][PL];                                    // prefetch ring of activation fragments
   auto aload = [&](int j, int slot) {
     const int o = ((kb0 + j) * QK + 8 * lg) * 2;
 #pragma unroll
-    for (int pl = 0; pl < PL; ++pl) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs[pl], voff[m] + o, 0, 0);
-        ra[slot][m][pl] = __builtin_bit_cast(h8, v);
-      }
-    }
+    for (int pl = 0; pl < PL; ++pl)
+      ra[slot][pl] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rs[pl], voff + o, 0, 0));
   };
 #pragma unroll
-  for (int j = 0; j < PDM; ++j)
+  for (int j = 0; j < PD; ++j)
     if (j < G::BPW) aload(j, j);
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int s = 0; s < G::NS; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < G::NS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < G::BPW; ++j) {
-    const int b = kb0 + j, slot = j % PDM;
+    const int b = kb0 + j, slot = j % PD;
     h8 bq[G::NS];
     float dsc[G::NS];
 #pragma unroll
@@ -122,46 +119,42 @@ __device__ inline void pass_tiles(const Args& p, const uint8_t* wl, const int* m
       bq[s] = gg::frag_codes<FMT>(rd, b, lg);
       dsc[s] = gg::frag_scale<FMT>(rd, b);
     }
-    h8 ah[MT], al[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      ah[m] = ra[slot][m][0];
-      if constexpr (SPLIT) al[m] = ra[slot][m][1];
-    }
-    if (j + PDM < G::BPW) aload(j + PDM, slot);
+    const h8 ah = ra[slot][0];
+    h8 al;
+    if constexpr (SPLIT) al = ra[slot][1];
+    if (j + PD < G::BPW) aload(j + PD, slot);
     // t = (a_hi [+ a_lo]) . q on the exact codes, then acc += d * t (the block's
     // scale of the lane's output column)
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int s = 0; s < G::NS; ++s) {
+      f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq[s], zero, 0, 0, 0);
+      if constexpr (SPLIT) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq[s], t, 0, 0, 0);
 #pragma unroll
-      for (int s = 0; s < G::NS; ++s) {
-        f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bq[s], zero, 0, 0, 0);
-        if constexpr (SPLIT) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[m], bq[s], t, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][s][i] = __builtin_fmaf(dsc[s], t[i], acc[m][s][i]);
-      }
+      for (int i = 0; i < 4; ++i) acc[s][i] = __builtin_fmaf(dsc[s], t[i], acc[s][i]);
+    }
   }
 }
 
-// (at least two waves per SIMD, i.e. two workgroups per CU: with fewer the
-// compiler spends more registers and one workgroup's slice load is not
-// covered by the other's MFMAs)
+// (three workgroups per CU for the 4-bit weights, two for Q8_0, whose slice
+// takes twice the LDS: each workgroup's slice copy and epilogue are covered by
+// the others' dots)
 template <int FMT, int STAGE, bool SPLIT>
-__global__ __launch_bounds__(NT, 2) void skinny_kernel(Args p) {
+__global__ __launch_bounds__(NT, FMT == MOE_FMT_Q4 ? 3 : 2) void skinny_kernel(Args p) {
   using G = Geo<FMT, STAGE>;
   __shared__ __attribute__((aligned(16))) uint8_t wl[G::W_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t red[G::RED_BYTES];
   __shared__ int m_src[MROWS];
   __shared__ int m_flat[MROWS];
-  __shared__ int act[E_MAX];                        // experts with rows, ascending
-  __shared__ int aoff[2 * E_MAX];                   // their clamped row ranges (lo, hi)
+  __shared__ int act[U_MAX];                        // 16-row units of experts with rows
+  __shared__ int aoff[2 * U_MAX];                   // their row ranges (lo, hi)
   __shared__ int n_act;
 
   const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE;
   const int ln = lane % 16, lg = lane / 16;
 
-  // ---- active experts (wavefront 0, in expert order) ----
+  // ---- units (wavefront 0, in expert order): an expert's rows split into 16-row
+  // units, so every item is one M-tile ----
   if (wave == 0) {
     int base = 0;
     for (int e0 = 0; e0 < p.E; e0 += WAVE) {
@@ -171,15 +164,20 @@ __global__ __launch_bounds__(NT, 2) void skinny_kernel(Args p) {
         lo = min(max(p.offsets[e], 0), p.R);
         hi = min(max(p.offsets[e + 1], lo), p.R);
       }
-      const bool on = e < p.E && hi > lo;
-      const uint64_t m = __ballot(on);
-      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-      if (on) {
-        act[pos] = e;
-        aoff[2 * pos] = lo;
-        aoff[2 * pos + 1] = hi;
+      const int nm = (hi - lo + 15) / 16;
+      int incl = nm;
+#pragma unroll
+      for (int off = 1; off < WAVE; off <<= 1) {
+        const int t = __shfl_up(incl, off, WAVE);
+        if (lane >= off) incl += t;
       }
-      base += __popcll(m);
+      const int pos = base + incl - nm;
+      for (int m = 0; m < nm; ++m) {
+        act[pos + m] = e;
+        aoff[2 * (pos + m)] = lo + 16 * m;
+        aoff[2 * (pos + m) + 1] = min(lo + 16 * (m + 1), hi);
+      }
+      base += __shfl(incl, WAVE - 1, WAVE);
     }
     if (lane == 0) n_act = base;
   }
@@ -208,9 +206,9 @@ __global__ __launch_bounds__(NT, 2) void skinny_kernel(Args p) {
         if (c0 + lane < G::RB / 16) gg::lds_dma16(src, 16u * (c0 + lane), wl + row * G::RBP + 16 * c0);
     }
 
-    for (int pass = 0; pass * MROWS < re; ++pass) {
+    {
       if (tid < MROWS) {
-        const int i = r0 + pass * MROWS + tid;
+        const int i = r0 + tid;
         int src = 0, fl = -1;
         if (i < r1) {
           const int f = p.rows[i];
@@ -222,51 +220,43 @@ __global__ __launch_bounds__(NT, 2) void skinny_kernel(Args p) {
         m_src[tid] = src;
         m_flat[tid] = fl;
       }
-      if (pass == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's slice rows
-      __syncthreads();                                // weights (first pass) and row metadata
-      f32x4 acc[2][G::NS];
-      const int nv = min(re - pass * MROWS, MROWS);
-      if (nv <= 16)
-        pass_tiles<FMT, STAGE, SPLIT, 1>(p, wl, m_src, kb0, lane, nv, acc);
-      else
-        pass_tiles<FMT, STAGE, SPLIT, 2>(p, wl, m_src, kb0, lane, nv, acc);
-      const int mt = nv <= 16 ? 1 : 2;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's slice rows
+      __syncthreads();                                // the slice and row metadata
+      f32x4 acc[G::NS];
+      pass_tile<FMT, STAGE, SPLIT>(p, wl, m_src, kb0, lane, re, acc);
 
       // ---- K quarters summed in wavefront order, epilogue by wavefront 0 ----
       f32x4* rd = (f32x4*)red;
       if (wave > 0) {
-        for (int m = 0; m < mt; ++m)
 #pragma unroll
-          for (int s = 0; s < G::NS; ++s) rd[(((wave - 1) * 2 + m) * G::NS + s) * WAVE + lane] = acc[m][s];
+        for (int s = 0; s < G::NS; ++s) rd[((wave - 1) * G::NS + s) * WAVE + lane] = acc[s];
       }
       __syncthreads();
       if (wave == 0) {
-        for (int m = 0; m < mt; ++m) {
 #pragma unroll
-          for (int w = 1; w < NW; ++w)
+        for (int w = 1; w < NW; ++w)
 #pragma unroll
-            for (int s = 0; s < G::NS; ++s) acc[m][s] += rd[(((w - 1) * 2 + m) * G::NS + s) * WAVE + lane];
-          // lane holds rows 16m + 4*lg + i, column ln of each n-subtile
+          for (int s = 0; s < G::NS; ++s) acc[s] += rd[((w - 1) * G::NS + s) * WAVE + lane];
+        // lane holds rows 4*lg + i, column ln of each n-subtile
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * m + 4 * lg + i;
-            const int fl = m_flat[r];
-            if (fl < 0) continue;                     // padding row
-            if constexpr (STAGE == STAGE_GATEUP) {
-              const int64_t o = (int64_t)(r0 + pass * MROWS + r) * G::N + n0 + ln;
-              const float hv = silu(acc[m][0][i]) * acc[m][1][i];
-              const _Float16 hh = (_Float16)hv;
-              p.ohi[o] = hh;
-              if constexpr (SPLIT) p.olo[o] = (_Float16)(hv - (float)hh);
-            } else {
-              float* yrow = p.y + (int64_t)fl * G::N + n0 + ln;
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * lg + i;
+          const int fl = m_flat[r];
+          if (fl < 0) continue;                       // padding row
+          if constexpr (STAGE == STAGE_GATEUP) {
+            const int64_t o = (int64_t)(r0 + r) * G::N + n0 + ln;
+            const float hv = silu(acc[0][i]) * acc[1][i];
+            const _Float16 hh = (_Float16)hv;
+            p.ohi[o] = hh;
+            if constexpr (SPLIT) p.olo[o] = (_Float16)(hv - (float)hh);
+          } else {
+            float* yrow = p.y + (int64_t)fl * G::N + n0 + ln;
 #pragma unroll
-              for (int s = 0; s < G::NS; ++s) yrow[16 * s] = acc[m][s][i];
-            }
+            for (int s = 0; s < G::NS; ++s) yrow[16 * s] = acc[s][i];
           }
         }
       }
-      __syncthreads();                                // metadata, partials and weights reused
+      __syncthreads();                                // metadata, partials and the slice reused
     }
   }
 }
