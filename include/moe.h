@@ -94,7 +94,9 @@ enum {
 /* Flags. */
 enum {
   MOE_F_RESIDUAL = 1,      /* out += layer input                                       */
-  MOE_F_DETERMINISTIC = 2, /* fp outputs bit-reproducible run to run                   */
+  MOE_F_DETERMINISTIC = 2, /* accepted, no effect: every path's fp outputs are already */
+                           /* bit-reproducible run to run (ordered sums, exact       */
+                           /* fixed-point accumulators)                              */
   MOE_F_PRENORM = 4,       /* moe_layer only: the layer input is rmsnorm(x, eps=1e-6)   */
   MOE_F_FP16_ACT = 8,      /* MFMA expert kernels: round activations to fp16 once       */
                            /* instead of carrying them as two fp16 terms (hi + lo); half */

@@ -115,50 +115,74 @@ hipError_t launch_down_generic(const float* h, const ExpertsDev& W, const int32_
 // With ids, a slot whose expert id is outside [0, E) was dropped by the
 // grouping: its y row was never computed, so it is skipped, and when y_out is
 // given its row there is set to zero (the value the header promises for a
-// dropped entry).
+// dropped entry).  With k <= KC every load a thread needs (ids, weights, the
+// k y rows, the residual) is issued before the first is used: one memory round
+// trip instead of one or two per slot.
+constexpr int CT = 64;                                 // threads per combine workgroup
+constexpr int KC = 8;                                  // slots loaded up front
+
 template <int V>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
-                                                      const float* __restrict__ w,
-                                                      const int32_t* __restrict__ ids, int E,
-                                                      float* __restrict__ y_out, int64_t T,
-                                                      int k, int D,
-                                                      const float* __restrict__ residual,
-                                                      const float* __restrict__ res_scale,
-                                                      float* __restrict__ out) {
+__global__ __launch_bounds__(CT) void combine_kernel(const float* __restrict__ y,
+                                                     const float* __restrict__ w,
+                                                     const int32_t* __restrict__ ids, int E,
+                                                     float* __restrict__ y_out, int64_t T,
+                                                     int k, int D,
+                                                     const float* __restrict__ residual,
+                                                     const float* __restrict__ res_scale,
+                                                     float* __restrict__ out) {
+  typedef float fv __attribute__((ext_vector_type(V)));
   const int64_t t = blockIdx.x;
-  const int d = (blockIdx.y * 256 + threadIdx.x) * V;
+  const int d = (blockIdx.y * CT + threadIdx.x) * V;
   if (d >= D) return;
-  float s[V] = {};
-  for (int j = 0; j < k; ++j) {
-    const int64_t r = t * k + j;
-    if (ids && (unsigned)ids[r] >= (unsigned)E) {
-      if (y_out) {
+  auto ld = [&](const float* a) { return *(const fv*)a; };
+  fv s = {};
+  if (k <= KC) {
+    int id[KC];
+    float wv[KC];
+    fv yv[KC];
 #pragma unroll
-        for (int i = 0; i < V; ++i) y_out[r * D + d + i] = 0.f;
+    for (int j = 0; j < KC; ++j) {
+      const int64_t r = t * k + min(j, k - 1);        // clamped: rows of this token
+      id[j] = ids ? ids[r] : 0;
+      wv[j] = w[r];
+      yv[j] = ld(y + r * D + d);                      // a dropped slot's row: read, not used
+    }
+    fv rv = {};
+    if (residual) rv = ld(residual + t * D + d);
+    const float rs = (residual && res_scale) ? res_scale[t] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      if (j >= k) break;
+      if (ids && (unsigned)id[j] >= (unsigned)E) {
+        if (y_out) *(fv*)(y_out + (t * k + j) * D + d) = fv{};
+        continue;
       }
-      continue;
-    }
-    const float wj = w[r];
-    const float* yr = y + r * D + d;
-    if constexpr (V == 4) {
-      const float4 v = *(const float4*)yr;
-      s[0] = fmaf(wj, v.x, s[0]);
-      s[1] = fmaf(wj, v.y, s[1]);
-      s[2] = fmaf(wj, v.z, s[2]);
-      s[3] = fmaf(wj, v.w, s[3]);
-    } else {
-      s[0] = fmaf(wj, yr[0], s[0]);
-    }
-  }
-  if (residual) {
-    const float rs = res_scale ? res_scale[t] : 1.0f;   // residual = rs * residual row
 #pragma unroll
-    for (int i = 0; i < V; ++i) s[i] += res_scale ? residual[t * D + d + i] * rs : residual[t * D + d + i];
+      for (int i = 0; i < V; ++i) s[i] = fmaf(wv[j], yv[j][i], s[i]);
+    }
+    if (residual) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) s[i] += res_scale ? rv[i] * rs : rv[i];
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int64_t r = t * k + j;
+      if (ids && (unsigned)ids[r] >= (unsigned)E) {
+        if (y_out) *(fv*)(y_out + r * D + d) = fv{};
+        continue;
+      }
+      const float wj = w[r];
+      const fv v = ld(y + r * D + d);
+#pragma unroll
+      for (int i = 0; i < V; ++i) s[i] = fmaf(wj, v[i], s[i]);
+    }
+    if (residual) {
+      const float rs = res_scale ? res_scale[t] : 1.0f;   // residual = rs * residual row
+#pragma unroll
+      for (int i = 0; i < V; ++i) s[i] += res_scale ? residual[t * D + d + i] * rs : residual[t * D + d + i];
+    }
   }
-  if constexpr (V == 4)
-    *(float4*)(out + t * D + d) = make_float4(s[0], s[1], s[2], s[3]);
-  else
-    out[t * D + d] = s[0];
+  *(fv*)(out + t * D + d) = s;
 }
 
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int D,
@@ -166,12 +190,12 @@ hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int 
                           const float* res_scale, const int32_t* ids, int E, float* y_out) {
   auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
   if (D % 4 == 0 && a16(y) && a16(out) && a16(residual) && a16(y_out)) {
-    dim3 grid((unsigned)T, (unsigned)((D / 4 + 255) / 256));
-    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, s, y, w, ids, E, y_out, T, k, D,
+    dim3 grid((unsigned)T, (unsigned)((D / 4 + CT - 1) / CT));
+    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(CT), 0, s, y, w, ids, E, y_out, T, k, D,
                        residual, res_scale, out);
   } else {
-    dim3 grid((unsigned)T, (unsigned)((D + 255) / 256));
-    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, s, y, w, ids, E, y_out, T, k, D,
+    dim3 grid((unsigned)T, (unsigned)((D + CT - 1) / CT));
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(CT), 0, s, y, w, ids, E, y_out, T, k, D,
                        residual, res_scale, out);
   }
   return hipGetLastError();
