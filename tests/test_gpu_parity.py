@@ -227,6 +227,21 @@ def test_many_token_shapes(T, E, fmt):
     check_out(g["out"], r["out"], f"T={T} E={E} every token")
 
 
+@pytest.mark.parametrize("fmt", [S.FMT_Q4, S.FMT_Q8_0])
+def test_weight_slice_experts_of_several_units(fmt):
+    """64 tokens x top-8 = 512 routed rows, the most the weight-slice kernels take;
+    the Zipf router gives several experts more than 32 rows (three or four 16-row
+    units each).  Routing and every token's output against the oracle."""
+    c = cases.router_case(f"units{fmt}", 264 + fmt, 64, 2048, 768, 128, 8, fmt, True, DEV)
+    g = run_layer(c, M.F_RESIDUAL)
+    logits = O.router_logits(c.x, c.G, c.b)
+    ids = O.select_topk(logits, c.k)
+    assert np.array_equal(g["ids"], ids), "expert ids differ"
+    assert np.bincount(ids.ravel(), minlength=c.E).max() > 32, "no expert of three or more units"
+    r = O.moe_layer(c.x, c.G, c.b, c.oracle_experts(prefetch=np.unique(ids)), c.k, residual=True)
+    check_out(g["out"], r["out"], f"64 tokens fmt={fmt} every token")
+
+
 @pytest.fixture(scope="module")
 def prefill_case():
     """1024-token Q8_0 layer at Qwen geometry, every token under the gap rule; the
@@ -258,6 +273,7 @@ def test_prefill_layer_every_token(prefill_case, flags):
     (4, 96, 64, 1, 1, 1),         # one expert, top-1: a dense SwiGLU FFN
     (7, 64, 32, 6, 6, 0),         # every expert selected
     (9, 160, 96, 40, 5, 1),       # odd geometry (generic kernels)
+    (6, 128, 64, 24, 12, 0),      # top-12: the ordered combine past its 8 preloaded slots
 ])
 def test_edge_shapes(T, D, F, E, k, fmt):
     c = cases.router_case(f"edge{T}", 100 + T, T, D, F, E, k, fmt, E > 8, DEV, host_experts=True)
