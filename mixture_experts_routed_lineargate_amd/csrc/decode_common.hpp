@@ -390,19 +390,18 @@ __device__ inline void load_dig(const uint8_t* dig, const float2* scl, int blk, 
 // (k rounds of a wave arg-max on one wavefront cost about 1.5 us per layer).
 // Another logit outranks e if it is larger, or equal with a lower index (the
 // router's tie-break), so the ranks are a strict total order and expert e is
-// selected iff rank(e) < K.  The caller has written lg[E] to LDS and set
-// top[j] = -1 for j < K (top 16-byte aligned), followed by a barrier.
-// Thread t (all NT = 4E threads) compares logit e = t / 4 with logits
+// selected iff rank(e) < K.  The caller has written lg[E] to LDS (16-byte
+// aligned) and set top[j] = -1 for j < K (top 16-byte aligned), followed by a
+// barrier.  Thread t (all NT = 4E threads) compares logit e = t / 4 with logits
 // 32*(t%4) .. +31.  The first pass counts only the logits >= lg[e]; less one
-// (e itself) that is rank(e) whenever no other logit equals lg[e].  A group of
-// m >= 2 equal logits below c larger ones all land on slot c + m - 1 and
-// leave slot c empty, so when all K slots are filled no tie reaches the top K
-// and the slots hold the exact ranks (a NaN logit counts nothing and takes no
-// slot).  Otherwise a second pass ranks with the full comparison; every
-// slot is then preset to its own index, so the selected ids are in [0, E)
-// whatever the logits hold.  Returns after a barrier, with sel_e / sel_w
-// holding the winners in ascending id and their renormalised softmax weights.
-__device__ inline void select_top8_block(const float* lg, int* top, int* sel_e, float* sel_w) {
+// (e itself) that is rank(e) whenever no other logit equals lg[e].  A group of m >= 2 equal logits below c
+// larger ones all land on slot c + m - 1 and leave slot c empty, so when all K
+// slots are filled no tie reaches the top K and the slots hold the exact ranks
+// (a NaN logit counts nothing and takes no slot).  Otherwise a second pass ranks
+// with the full comparison; every slot is then preset to its own index,
+// so the selected ids are in [0, E) whatever the logits hold.  Returns after a
+// barrier with the slots final, as 8 wavefront-uniform ids in rank order.
+__device__ inline void top8_slots(const float* lg, int* top, int (&t)[K]) {
   static_assert(NT == 4 * E, "four threads per logit");
   static_assert(K == 8, "the slots are read as two int4");
   const int tid = threadIdx.x;
@@ -441,13 +440,33 @@ __device__ inline void select_top8_block(const float* lg, int* top, int* sel_e, 
     ta = *(const int4*)top;
     tb = *(const int4*)(top + 4);
   }
-  if (tid < WAVE) {
-    // the slots are the same in every lane: lane j < K takes winner j (rank
-    // order); the sum runs over the 8 lanes in a fixed tree order, so every
-    // workgroup gets the same bits
-    int t[K] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+  const int v[K] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-    for (int r = 0; r < K; ++r) t[r] = __builtin_amdgcn_readfirstlane(min(max(t[r], 0), E - 1));
+  for (int r = 0; r < K; ++r) t[r] = __builtin_amdgcn_readfirstlane(min(max(v[r], 0), E - 1));
+}
+
+// The id of slot j of the winners in ascending id order (t in rank order, as
+// top8_slots returns it): lane r < K ranks winner r among the 8, one ballot
+// finds the lane whose rank is j (the ids are distinct).
+__device__ inline int top8_ascending(const int (&t)[K], int j) {
+  const int lane = threadIdx.x % WAVE;
+  int tl = t[0];
+#pragma unroll
+  for (int r = 1; r < K; ++r) tl = (lane & (K - 1)) == r ? t[r] : tl;
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < K; ++q) c += t[q] < tl;
+  const uint64_t m = __ballot(lane < K && min(c, K - 1) == j);
+  return m ? __builtin_amdgcn_readlane(tl, __builtin_ctzll(m)) : t[j];
+}
+
+// Wavefront 0: sel_e / sel_w = the winners in ascending id and their
+// renormalised softmax weights (lane j < K takes winner j in rank order; the
+// sum runs over the 8 lanes in a fixed tree order, so every workgroup gets the
+// same bits).  Readers need a barrier after it.
+__device__ inline void top8_weights(const float* lg, const int (&t)[K], int* sel_e, float* sel_w) {
+  const int tid = threadIdx.x;
+  if (tid < WAVE) {
     const int j = tid & (K - 1);
     int me = t[0];
 #pragma unroll
@@ -463,7 +482,6 @@ __device__ inline void select_top8_block(const float* lg, int* top, int* sel_e, 
       sel_w[pos] = ex * __builtin_amdgcn_rcpf(den);
     }
   }
-  __syncthreads();
 }
 
 }  // namespace dec

@@ -284,10 +284,12 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
       if (lane == 0) s_inv = inv;
     }
     __syncthreads();
-    select_top8_block(lg, top, sel_e, sel_w);
+    int win[K];
+    top8_slots(lg, top, win);
     const float inv = s_inv;
-    const int e_j = min(max(sel_e[slot], 0), E - 1);
-    const float w_j = sel_w[slot];
+    // the weight stream needs only this slot's expert; the weights are formed
+    // once the stream is on its way
+    const int e_j = top8_ascending(win, slot);
     // in_l over this part's rows: slot 0 adds it to o_l
     const float in_row = (slot == 0 && p.residual && tid < DPW) ? xs[dr0 + tid] * inv : 0.f;
     // ---- W + H: stream the weight share two groups ahead of the gate/up dots ----
@@ -314,6 +316,7 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
     u32x4 dn[G::DN_ITERS];
     load_group(0, ga);
     load_group(1, gb);
+    top8_weights(lg, win, sel_e, sel_w);            // published by the barrier below
 
     // x = in_l = inv * o as digit planes (all threads, LDS past xs), then this
     // lane's block (block `lane` of the 2048-wide input) into registers
@@ -321,6 +324,7 @@ __global__ __launch_bounds__(NT, 1) void decode_stack_kernel(StackArgs p) {
     float2* xscl = (float2*)(lds + D * 4 + (D / QK) * 96);
     act_digits_lds<FMT, 4>(xs, inv, D / QK, xdig, xscl);
     __syncthreads();
+    const float w_j = sel_w[slot];
     ActDig xd;
     load_dig(xdig, xscl, lane, xd);
     __syncthreads();                                  // xs consumed
