@@ -405,7 +405,7 @@ __global__ __launch_bounds__(NT, wg_per_cu<SPLIT>()) void grouped_gemm_kernel(Ar
             if constexpr (STAGE == STAGE_GATEUP) {
 #pragma unroll
               for (int s = 0; s < 2; ++s) {
-                const int64_t o = (int64_t)(row0 + r) * p.N + n0 + wave * 32 + s * 16 + ln;
+                const int64_t o = (int64_t)(row0 + r) * p.N + plane_pos(n0 + wave * 32 + s * 16 + ln);
                 const float hv = silu(acc[m][s][i]) * acc[m][s + 2][i];
                 const _Float16 hh = (_Float16)hv;
                 p.ohi[o] = hh;
@@ -550,29 +550,30 @@ hipError_t launch_grouped_down(const _Float16* hhi, const _Float16* hlo, int a_m
                                : gg::launch_f<MOE_FMT_Q4, gg::STAGE_DOWN>(p, R, sm, split, s);
 }
 
-// hi = fp16(v), lo = fp16(v - hi) for n values (n % 4 == 0, 16-byte aligned)
-__global__ __launch_bounds__(256) void to_planes_kernel(const float* __restrict__ src, int64_t n4,
+// hi = fp16(v), lo = fp16(v - hi) for n values (n % 8 == 0, 16-byte aligned), each
+// group of 8 in the planes' order (plane_pos)
+__global__ __launch_bounds__(256) void to_planes_kernel(const float* __restrict__ src, int64_t n8,
                                                         _Float16* __restrict__ hi,
                                                         _Float16* __restrict__ lo) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const float4 v = ((const float4*)src)[i];
-  const float a[4] = {v.x, v.y, v.z, v.w};
-  gg::h4 h, l;
+  if (i >= n8) return;
+  const float4 v0 = ((const float4*)src)[2 * i], v1 = ((const float4*)src)[2 * i + 1];
+  const float a[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  gg::h8 h, l;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    h[j] = (_Float16)a[j];
-    l[j] = (_Float16)(a[j] - (float)h[j]);
+  for (int k = 0; k < 8; ++k) {
+    h[plane_pos(k)] = (_Float16)a[k];
+    l[plane_pos(k)] = (_Float16)(a[k] - (float)h[plane_pos(k)]);
   }
-  ((gg::h4*)hi)[i] = h;
-  if (lo) ((gg::h4*)lo)[i] = l;
+  ((gg::h8*)hi)[i] = h;
+  if (lo) ((gg::h8*)lo)[i] = l;
 }
 
 hipError_t launch_to_planes(const float* src, int64_t n, _Float16* hi, _Float16* lo,
                             hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const int64_t n4 = n / 4;
-  hipLaunchKernelGGL(to_planes_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, src, n4,
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(to_planes_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, src, n8,
                      hi, lo);
   return hipGetLastError();
 }

@@ -113,6 +113,17 @@ struct Workspace {
 
 int router_ksplit(int64_t T, int D);
 Workspace carve_workspace(void* base, int64_t T, int D, int F, int E, int k, int flags);
+// Activation planes (the fp16 hi / lo rows of x or h that the MFMA expert kernels
+// read) hold each group of 8 consecutive values in the order 0, 2, 4, 6, 1, 3, 5, 7:
+// the order in which one byte permute per pair rebuilds a block's codes as fp16
+// (the low, then the high nibbles of four bytes; the even, then the odd bytes of
+// two dwords).  plane_pos(k) is the position of value k in its row.
+__host__ __device__ constexpr int plane_pos(int k) {
+  return (k & ~7) | ((k & 1) << 2) | ((k & 7) >> 1);
+}
+static_assert(plane_pos(1) == 4 && plane_pos(2) == 1 && plane_pos(7) == 7 && plane_pos(14) == 11,
+              "plane order");
+
 constexpr size_t SYNC_BYTES = 4 * 1024 * 1024;  // barrier words and exchange buffers
 constexpr size_t ROUTE_SYNC_OFF = 2 * 1024 * 1024;  // small-batch routing's exchange words
 constexpr size_t STACK_ACC_OFF = 1280 * 1024;      // decode stack accumulators (written by no other kernel)

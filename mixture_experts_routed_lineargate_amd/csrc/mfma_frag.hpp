@@ -1,7 +1,9 @@
 // Weight fragments for v_mfma_f32_16x16x32_f16 built from block-quantized rows
 // (shared by the grouped GEMM kernels).  A lane of a B fragment holds the 8
 // weights k = 8g .. 8g+7 of one weight row within a 32-value block, as their
-// exact integer codes; the block's fp16 scale is applied to the MFMA result.
+// exact integer codes, in the activation planes' order (8g + 0, 2, 4, 6, 1, 3, 5,
+// 7: plane_pos), so that the A fragment read from a plane row pairs each code with
+// its own activation; the block's fp16 scale is applied to the MFMA result.
 // frag_codes / frag_scale read a row staged in LDS through `rd(off)` (the dword
 // at byte offset `off`, a multiple of 4, of the stored row); codes_q8 / codes_q4
 // turn code dwords into fp16 fragments; lds_dma16 streams 16-byte pieces from
@@ -17,7 +19,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
-// Eight signed Q8_0 codes (bytes of q0, then q1) as exact fp16 values.
+// Eight signed Q8_0 codes b0..b7 (bytes of q0, then q1) as exact fp16 values, in
+// the order b0 b2 b4 b6 b1 b3 b5 b7.
 __device__ inline h8 codes_q8(uint32_t q0, uint32_t q1) {
   union {
     uint32_t u[4];
@@ -27,18 +30,20 @@ __device__ inline h8 codes_q8(uint32_t q0, uint32_t q1) {
   // two's complement -> biased unsigned, then 0x64uu = 1024 + u as fp16
   q0 ^= 0x80808080u;
   q1 ^= 0x80808080u;
-  r.u[0] = __builtin_amdgcn_perm(0x64646464u, q0, 0x04010400u);
-  r.u[1] = __builtin_amdgcn_perm(0x64646464u, q0, 0x04030402u);
-  r.u[2] = __builtin_amdgcn_perm(0x64646464u, q1, 0x04010400u);
-  r.u[3] = __builtin_amdgcn_perm(0x64646464u, q1, 0x04030402u);
+  r.u[0] = __builtin_amdgcn_perm(0x64646464u, q0, 0x04020400u);   // b0 b2
+  r.u[1] = __builtin_amdgcn_perm(0x64646464u, q1, 0x04020400u);   // b4 b6
+  r.u[2] = __builtin_amdgcn_perm(0x64646464u, q0, 0x04030401u);   // b1 b3
+  r.u[3] = __builtin_amdgcn_perm(0x64646464u, q1, 0x04030401u);   // b5 b7
   const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};   // 1024 + 128
 #pragma unroll
   for (int i = 0; i < 4; ++i) r.p[i] = r.p[i] - bias;
   return r.v;
 }
 
-// Eight 4-bit codes (byte j holds element 2j in its low nibble, 2j+1 in its
-// high nibble) as the exact fp16 values q - 8.
+// Eight 4-bit codes q0..q7 (byte j holds q_2j in its low nibble, q_2j+1 in its
+// high nibble) as the exact fp16 values q - 8, in the order q0 q2 q4 q6 q1 q3 q5
+// q7: the low nibbles of the four bytes, then the high ones, each pair placed
+// under a 0x64 exponent byte by one permute.
 __device__ inline h8 codes_q4(uint32_t n) {
   union {
     uint32_t u[4];
@@ -46,10 +51,10 @@ __device__ inline h8 codes_q4(uint32_t n) {
     h8 v;
   } r;
   const uint32_t lo = n & 0x0f0f0f0fu, hi = (n >> 4) & 0x0f0f0f0fu;
-  r.u[0] = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x64006400u;
-  r.u[1] = __builtin_amdgcn_perm(hi, lo, 0x0c050c01u) | 0x64006400u;
-  r.u[2] = __builtin_amdgcn_perm(hi, lo, 0x0c060c02u) | 0x64006400u;
-  r.u[3] = __builtin_amdgcn_perm(hi, lo, 0x0c070c03u) | 0x64006400u;
+  r.u[0] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u);   // q0 q2
+  r.u[1] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u);   // q4 q6
+  r.u[2] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u);   // q1 q3
+  r.u[3] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u);   // q5 q7
   const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};   // 1024 + 8
 #pragma unroll
   for (int i = 0; i < 4; ++i) r.p[i] = r.p[i] - bias;

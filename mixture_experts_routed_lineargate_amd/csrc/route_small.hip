@@ -250,8 +250,8 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
         p.w[b * k + rank] = ex / den;
       }
     }
-    // input planes of token b (element by element: a packed conversion would round
-    // ties unlike the other kernels that write planes)
+    // input planes of token b, in the planes' order (element by element: a packed
+    // conversion would round ties unlike the other kernels that write planes)
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
       const int d = 4 * (j * NT + tid);
@@ -260,8 +260,8 @@ __global__ __launch_bounds__(NT) void route_small_kernel(Args p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const _Float16 hi = (_Float16)u[i];
-        p.xhi[(int64_t)b * D + d + i] = hi;
-        if (p.xlo) p.xlo[(int64_t)b * D + d + i] = (_Float16)(u[i] - (float)hi);
+        p.xhi[(int64_t)b * D + plane_pos(d + i)] = hi;
+        if (p.xlo) p.xlo[(int64_t)b * D + plane_pos(d + i)] = (_Float16)(u[i] - (float)hi);
       }
     }
     __syncthreads();                                  // sids written by wavefront 0

@@ -283,10 +283,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
           lo[i] = (_Float16)(u[i] - (float)hi[i]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ex.xhi[t * ex.D + d + i] = hi[i];
+        for (int i = 0; i < 4; ++i) ex.xhi[t * ex.D + plane_pos(d + i)] = hi[i];
         if (ex.xlo) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ex.xlo[t * ex.D + d + i] = lo[i];
+          for (int i = 0; i < 4; ++i) ex.xlo[t * ex.D + plane_pos(d + i)] = lo[i];
         }
       }
     }
@@ -344,10 +344,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
           lo[i] = (_Float16)(u[i] - (float)hi[i]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ex.xhi[t * ex.D + d + i] = hi[i];
+        for (int i = 0; i < 4; ++i) ex.xhi[t * ex.D + plane_pos(d + i)] = hi[i];
         if (ex.xlo) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ex.xlo[t * ex.D + d + i] = lo[i];
+          for (int i = 0; i < 4; ++i) ex.xlo[t * ex.D + plane_pos(d + i)] = lo[i];
         }
       }
     }

@@ -244,7 +244,7 @@ __global__ __launch_bounds__(NT, FMT == MOE_FMT_Q4 ? 3 : 2) void skinny_kernel(A
           const int fl = m_flat[r];
           if (fl < 0) continue;                       // padding row
           if constexpr (STAGE == STAGE_GATEUP) {
-            const int64_t o = (int64_t)(r0 + r) * G::N + n0 + ln;
+            const int64_t o = (int64_t)(r0 + r) * G::N + plane_pos(n0 + ln);
             const float hv = silu(acc[0][i]) * acc[1][i];
             const _Float16 hh = (_Float16)hv;
             p.ohi[o] = hh;
