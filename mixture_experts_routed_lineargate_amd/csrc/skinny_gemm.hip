@@ -58,7 +58,7 @@ struct Geo {
   static constexpr int NCB = N / COLS;            // workgroups per expert
   static constexpr int BPW = K / QK / NW;         // blocks per wavefront
   static constexpr int W_BYTES = WR * RBP;
-  static constexpr int RED_BYTES = (NW - 1) * NS * WAVE * 16;
+  static_assert(NW * NS * WAVE * 16 <= W_BYTES, "partial tiles fit in the slice's LDS");
   static_assert(RB % 16 == 0 && (RBP / 16) % 2 == 1, "row stride");
   static_assert(K % (QK * NW) == 0 && N % COLS == 0, "shape");
 };
@@ -143,7 +143,6 @@ template <int FMT, int STAGE, bool SPLIT>
 __global__ __launch_bounds__(NT, FMT == MOE_FMT_Q4 ? 3 : 2) void skinny_kernel(Args p) {
   using G = Geo<FMT, STAGE>;
   __shared__ __attribute__((aligned(16))) uint8_t wl[G::W_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t red[G::RED_BYTES];
   __shared__ int m_src[MROWS];
   __shared__ int m_flat[MROWS];
   __shared__ int act[U_MAX];                        // 16-row units of experts with rows
@@ -225,34 +224,37 @@ __global__ __launch_bounds__(NT, FMT == MOE_FMT_Q4 ? 3 : 2) void skinny_kernel(A
       f32x4 acc[G::NS];
       pass_tile<FMT, STAGE, SPLIT>(p, wl, m_src, kb0, lane, re, acc);
 
-      // ---- K quarters summed in wavefront order, epilogue by wavefront 0 ----
-      f32x4* rd = (f32x4*)red;
-      if (wave > 0) {
+      // ---- K quarters summed in wavefront order, four rows per wavefront ----
+      // The partial tiles go to the slice's LDS (free once every wavefront has passed
+      // over it).  Wavefront w then takes rows 4w .. 4w+3: its lane (c, i) holds
+      // element i of lane c + 16w of each wavefront's partial, i.e. row 4w + i,
+      // column c, and adds the four in wavefront order.
+      __syncthreads();                                // every wavefront is done with the slice
+      f32x4* rd = (f32x4*)wl;
 #pragma unroll
-        for (int s = 0; s < G::NS; ++s) rd[((wave - 1) * G::NS + s) * WAVE + lane] = acc[s];
-      }
+      for (int s = 0; s < G::NS; ++s) rd[(wave * G::NS + s) * WAVE + lane] = acc[s];
       __syncthreads();
-      if (wave == 0) {
+      {
+        const int c = lane % 16, i = lane / 16, r = 4 * wave + i;
+        float v[G::NS];
 #pragma unroll
-        for (int w = 1; w < NW; ++w)
+        for (int s = 0; s < G::NS; ++s) {
+          v[s] = rd[s * WAVE + c + 16 * wave][i];
 #pragma unroll
-          for (int s = 0; s < G::NS; ++s) acc[s] += rd[((w - 1) * G::NS + s) * WAVE + lane];
-        // lane holds rows 4*lg + i, column ln of each n-subtile
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * lg + i;
-          const int fl = m_flat[r];
-          if (fl < 0) continue;                       // padding row
+          for (int w = 1; w < NW; ++w) v[s] += rd[(w * G::NS + s) * WAVE + c + 16 * wave][i];
+        }
+        const int fl = m_flat[r];
+        if (fl >= 0) {                                // else a padding row
           if constexpr (STAGE == STAGE_GATEUP) {
-            const int64_t o = (int64_t)(r0 + r) * G::N + plane_pos(n0 + ln);
-            const float hv = silu(acc[0][i]) * acc[1][i];
+            const int64_t o = (int64_t)(r0 + r) * G::N + plane_pos(n0 + c);
+            const float hv = silu(v[0]) * v[1];
             const _Float16 hh = (_Float16)hv;
             p.ohi[o] = hh;
             if constexpr (SPLIT) p.olo[o] = (_Float16)(hv - (float)hh);
           } else {
-            float* yrow = p.y + (int64_t)fl * G::N + n0 + ln;
+            float* yrow = p.y + (int64_t)fl * G::N + n0 + c;
 #pragma unroll
-            for (int s = 0; s < G::NS; ++s) yrow[16 * s] = acc[s][i];
+            for (int s = 0; s < G::NS; ++s) yrow[16 * s] = v[s];
           }
         }
       }
