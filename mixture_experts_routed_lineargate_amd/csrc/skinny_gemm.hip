@@ -19,7 +19,7 @@
 // LDS with a stride that is an odd multiple of 16 bytes, which puts the 16 rows
 // x 4 lane groups of a fragment read in distinct banks.  The grid is
 // persistent: every workgroup builds the list of units from expert_offsets (in
-// LDS) and walks the (unit, slice) items with a stride of the grid size.
+// LDS) and takes (unit, slice) items in rounds over the grid.
 //
 // Why units of one M-tile: a hot expert's 17-32 rows as one two-tile item took
 // well over twice a one-tile item (the prefetch ring is half as deep per tile),
@@ -184,7 +184,16 @@ __global__ __launch_bounds__(NT, FMT == MOE_FMT_Q4 ? 3 : 2) void skinny_kernel(A
   const int items = n_act * G::NCB;
   const int kb0 = wave * G::BPW;                    // this wavefront's first block
 
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+  // Items go out in rounds over the grid, every third round to its first third
+  // only: the first workgroups dispatched, one per CU, are the oldest on their CU and
+  // issue first, so they finish items sooner than the CU's later ones (an even walk
+  // left those last by ~10 us).
+  int base = 0;
+  for (int r = 0; base < items; ++r) {
+    const int width = r % 3 == 2 ? max((int)gridDim.x / 3, 1) : (int)gridDim.x;
+    const int it = base + (int)blockIdx.x;
+    base += width;
+    if ((int)blockIdx.x >= width || it >= items) continue;   // uniform over the workgroup
     const int u = it / G::NCB, cb = it % G::NCB;
     const int e = act[u], r0 = aoff[2 * u], r1 = aoff[2 * u + 1], re = r1 - r0;
 
