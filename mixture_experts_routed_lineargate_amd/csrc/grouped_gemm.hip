@@ -210,8 +210,18 @@ __global__ __launch_bounds__(NT, wg_per_cu<SPLIT>()) void grouped_gemm_kernel(Ar
   __syncthreads();
   const int total = total_m * p.n_tiles;
   const int G = gridDim.x;
+  // Whole rounds of G tiles, then a partial round.  In a whole round workgroup b
+  // takes position xcd_swizzle(b) (an XCD's workgroups take consecutive tiles).
+  // The partial round goes first to the older half of the grid (blockIdx < G/2,
+  // dispatched first, one per CU): a CU issues its older workgroup's waves first,
+  // so those finish their tiles sooner.
   const int first = xcd_swizzle(blockIdx.x, G);
-  const int ntiles = (total - first + G - 1) / G;
+  const int rounds = total / G, rest = total - rounds * G;
+  const int half = G / 2;
+  const int last = (int)blockIdx.x < half ? xcd_swizzle(blockIdx.x, half)
+                                          : half + xcd_swizzle(blockIdx.x - half, G - half);
+  const int ntiles = rounds + (last < rest ? 1 : 0);
+  auto wpos = [&](int k) { return k < rounds ? first + k * G : rounds * G + last; };
   const int64_t RB = (int64_t)(p.K / QK) * LR::BB;  // bytes per stored weight row
   const int nchunks = p.K / BK;                     // even (K is a multiple of 128)
 
@@ -255,7 +265,7 @@ __global__ __launch_bounds__(NT, wg_per_cu<SPLIT>()) void grouped_gemm_kernel(Ar
       int src = 0, fl = -1;
       if (w < TW && k0 + w < ntiles) {
         int e, row0, nrows, nt;
-        decode_tile(first + (k0 + w) * G, e, row0, nrows, nt);
+        decode_tile(wpos(k0 + w), e, row0, nrows, nt);
         if (r < nrows) {
           const int i = row0 + r;
           const int f = p.rows[i];
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(NT, wg_per_cu<SPLIT>()) void grouped_gemm_kernel(Ar
     for (int w = 0; w < TW; ++w) {
       if (k0 + w >= ntiles) break;                    // uniform over the workgroup
       int e, row0, nrows, nt;
-      decode_tile(first + (k0 + w) * G, e, row0, nrows, nt);
+      decode_tile(wpos(k0 + w), e, row0, nrows, nt);
       e = __builtin_amdgcn_readfirstlane(e);          // the tile is the workgroup's: make its
       row0 = __builtin_amdgcn_readfirstlane(row0);    // fields scalar so every address below
       nrows = __builtin_amdgcn_readfirstlane(nrows);  // is a scalar base + lane offset
