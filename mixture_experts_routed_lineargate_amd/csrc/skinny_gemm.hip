@@ -25,9 +25,10 @@
 // well over twice a one-tile item (the prefetch ring is half as deep per tile),
 // two such items on one CU set the end of the launch, and the two-tile code
 // kept the kernel at two workgroups per CU.  With one tile the 4-bit kernels fit
-// three workgroups per CU (registers and LDS), and each CU keeps three items'
-// slice copies and dots in flight; the units of a slice read the same weight
-// bytes, which the caches serve after the first.
+// three workgroups per CU (registers and LDS; the 4-bit down kernel, with its
+// 28 KB slice, fits four), and each CU keeps that many items' slice copies and
+// dots in flight; the units of a slice read the same weight bytes, which the
+// caches serve after the first.
 #include "mfma_frag.hpp"
 
 namespace moe {
