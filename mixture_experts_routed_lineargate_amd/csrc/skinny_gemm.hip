@@ -25,10 +25,9 @@
 // well over twice a one-tile item (the prefetch ring is half as deep per tile),
 // two such items on one CU set the end of the launch, and the two-tile code
 // kept the kernel at two workgroups per CU.  With one tile the 4-bit kernels fit
-// three workgroups per CU (registers and LDS; the 4-bit down kernel, with its
-// 28 KB slice, fits four), and each CU keeps that many items' slice copies and
-// dots in flight; the units of a slice read the same weight bytes, which the
-// caches serve after the first.
+// four workgroups per CU (128 registers, at most 40 KB of LDS), and each CU keeps
+// four items' slice copies and dots in flight; the units of a slice read the
+// same weight bytes, which the caches serve after the first.
 #include "mfma_frag.hpp"
 
 namespace moe {
@@ -38,7 +37,6 @@ using gg::h8;
 constexpr int NT = 256;       // 4 wavefronts
 constexpr int NW = NT / WAVE;
 constexpr int MROWS = 16;     // rows per item (one M-tile)
-constexpr int PD = 8;         // activation-fragment prefetch depth (blocks)
 constexpr int D_TUNED = 2048, F_TUNED = 768;
 constexpr int E_MAX = 256;    // experts per layer this kernel takes
 constexpr int U_MAX = E_MAX + 512 / 16;   // 16-row units: at most one per expert + one per 16 rows
@@ -96,6 +94,9 @@ __device__ inline void pass_tile(const Args& p, const uint8_t* wl, const int* m_
       __builtin_amdgcn_make_buffer_rsrc((void*)p.ahi, 0, NREC, 0x00020000),
       __builtin_amdgcn_make_buffer_rsrc((void*)p.alo, 0, NREC, 0x00020000)};
   const int voff = ln < nv ? m_src[ln] * G::K * 2 : NREC;
+  // activation-fragment prefetch depth (blocks): 4 for the 4-bit gate/up stage, so that
+  // it fits 128 registers and four workgroups per CU
+  constexpr int PD = (FMT == MOE_FMT_Q4 && STAGE == STAGE_GATEUP) ? 4 : 8;
   h8 ra[PD][PL];                                    // prefetch ring of activation fragments
   auto aload = [&](int j, int slot) {
     const int o = ((kb0 + j) * QK + 8 * lg) * 2;
@@ -137,16 +138,16 @@ __device__ inline void pass_tile(const Args& p, const uint8_t* wl, const int* m_
   }
 }
 
-// (three workgroups per CU for the 4-bit weights, two for Q8_0, whose slice
+// (four workgroups per CU for the 4-bit weights, two for Q8_0, whose slice
 // takes twice the LDS: each workgroup's slice copy and epilogue are covered by
 // the others' dots)
 template <int FMT, int STAGE, bool SPLIT>
-__global__ __launch_bounds__(NT, FMT == MOE_FMT_Q4 ? 3 : 2) void skinny_kernel(Args p) {
+__global__ __launch_bounds__(NT, FMT == MOE_FMT_Q4 ? 4 : 2) void skinny_kernel(Args p) {
   using G = Geo<FMT, STAGE>;
   __shared__ __attribute__((aligned(16))) uint8_t wl[G::W_BYTES];
   __shared__ int m_src[MROWS];
   __shared__ int m_flat[MROWS];
-  __shared__ int act[U_MAX];                        // 16-row units of experts with rows
+  __shared__ uint8_t act[U_MAX];                    // 16-row units of experts with rows
   __shared__ int aoff[2 * U_MAX];                   // their row ranges (lo, hi)
   __shared__ int n_act;
 
