@@ -186,13 +186,13 @@ __global__ __launch_bounds__(NT, FMT == MOE_FMT_Q4 ? 4 : 2) void skinny_kernel(A
   const int items = n_act * G::NCB;
   const int kb0 = wave * G::BPW;                    // this wavefront's first block
 
-  // Items go out in rounds over the grid, every third round to its first third
-  // only: the first workgroups dispatched, one per CU, are the oldest on their CU and
-  // issue first, so they finish items sooner than the CU's later ones (an even walk
-  // left those last by ~10 us).
+  // Items go out in rounds over the grid, every other round to its first half
+  // only: the first workgroups dispatched (one or two per CU) are the oldest on
+  // their CU and issue first, so they finish items sooner than the CU's later ones
+  // (an even walk left those last by ~10 us).
   int base = 0;
   for (int r = 0; base < items; ++r) {
-    const int width = r % 3 == 2 ? max((int)gridDim.x / 3, 1) : (int)gridDim.x;
+    const int width = r % 2 == 1 ? max((int)gridDim.x / 2, 1) : (int)gridDim.x;
     const int it = base + (int)blockIdx.x;
     base += width;
     if ((int)blockIdx.x >= width || it >= items) continue;   // uniform over the workgroup
