@@ -112,7 +112,7 @@ __device__ inline void gather_finish(uint64_t* v, AddrFn addr, uint32_t t, uint3
     for (int i = 0; i < N; ++i) ready &= (uint32_t)(v[i] >> 32) == t;
     if (ready) break;
     if (budget == 0) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // keeps bit 1
       timed_out = true;
       break;
     }

@@ -122,12 +122,51 @@ struct LdsRow<MOE_FMT_Q4> {
   }
 };
 
-__device__ inline int xcd_swizzle(int bid, int total) {
+__host__ __device__ constexpr int xcd_swizzle(int bid, int total) {
   // bid = 8 s + x runs on XCD x; give XCD x a contiguous range of tiles
   const int x = bid & 7, s = bid >> 3;
   const int q = total >> 3, r = total & 7;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + s;
 }
+
+// The tile walk of a G-workgroup grid over `total` tiles: whole rounds of G
+// tiles, workgroup b taking position xcd_swizzle(b, G) in each, then a partial
+// round whose positions go first to the older half of the grid (b < G/2).
+struct TileWalk {
+  int G, first, last, rounds, rest;
+  __host__ __device__ constexpr TileWalk(int b, int g, int total)
+      : G(g), first(xcd_swizzle(b, g)),
+        last(b < g / 2 ? xcd_swizzle(b, g / 2) : g / 2 + xcd_swizzle(b - g / 2, g - g / 2)),
+        rounds(total / g), rest(total - total / g * g) {}
+  __host__ __device__ constexpr int count() const { return rounds + (last < rest ? 1 : 0); }
+  __host__ __device__ constexpr int pos(int k) const { return k < rounds ? first + k * G : rounds * G + last; }
+};
+
+// Checked at compile time for the grid sizes below: the walk hands out every
+// tile exactly once.
+constexpr bool walk_exact(int G, int total) {
+  constexpr int CAP = 4096;
+  bool seen[CAP] = {};
+  if (G < 1 || total < 0 || total > CAP) return false;
+  int n = 0;
+  for (int b = 0; b < G; ++b) {
+    const TileWalk w(b, G, total);
+    for (int k = 0; k < w.count(); ++k) {
+      const int t = w.pos(k);
+      if (t < 0 || t >= total || seen[t]) return false;
+      seen[t] = true;
+      ++n;
+    }
+  }
+  return n == total;
+}
+static_assert(walk_exact(1, 0) && walk_exact(1, 5) && walk_exact(2, 3) && walk_exact(3, 7) &&
+                  walk_exact(7, 50) && walk_exact(9, 9) && walk_exact(13, 100) &&
+                  walk_exact(256, 255) && walk_exact(512, 0) && walk_exact(512, 511) &&
+                  walk_exact(512, 513) && walk_exact(512, 1400) && walk_exact(510, 4096) &&
+                  walk_exact(1024, 3000) && walk_exact(511, 700) && walk_exact(1023, 2000) &&
+                  walk_exact(257, 4096),
+              "tile walk");
 
 // Compute units of the current device (cached per device).
 static int device_cus() {
@@ -210,18 +249,13 @@ __global__ __launch_bounds__(NT, wg_per_cu<SPLIT>()) void grouped_gemm_kernel(Ar
   __syncthreads();
   const int total = total_m * p.n_tiles;
   const int G = gridDim.x;
-  // Whole rounds of G tiles, then a partial round.  In a whole round workgroup b
-  // takes position xcd_swizzle(b) (an XCD's workgroups take consecutive tiles).
-  // The partial round goes first to the older half of the grid (blockIdx < G/2,
-  // dispatched first, one per CU): a CU issues its older workgroup's waves first,
-  // so those finish their tiles sooner.
-  const int first = xcd_swizzle(blockIdx.x, G);
-  const int rounds = total / G, rest = total - rounds * G;
-  const int half = G / 2;
-  const int last = (int)blockIdx.x < half ? xcd_swizzle(blockIdx.x, half)
-                                          : half + xcd_swizzle(blockIdx.x - half, G - half);
-  const int ntiles = rounds + (last < rest ? 1 : 0);
-  auto wpos = [&](int k) { return k < rounds ? first + k * G : rounds * G + last; };
+  // Whole rounds of G tiles, then a partial round (TileWalk).  In a whole round an
+  // XCD's workgroups take consecutive tiles.  The partial round goes first to the
+  // older half of the grid (blockIdx < G/2, dispatched first, one per CU): a CU
+  // issues its older workgroup's waves first, so those finish their tiles sooner.
+  const TileWalk walk(blockIdx.x, G, total);
+  const int ntiles = walk.count();
+  auto wpos = [&](int k) { return walk.pos(k); };
   const int64_t RB = (int64_t)(p.K / QK) * LR::BB;  // bytes per stored weight row
   const int nchunks = p.K / BK;                     // even (K is a multiple of 128)
 
