@@ -182,8 +182,12 @@ def cpu_decode(arena, layers_np, budget_s: float):
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def graph_time_ms(torch, fn, stream, warmup: int, iters: int) -> float:
-    """Capture fn() once as a HIP graph; return the mean ms per replay (events on `stream`)."""
+REPEATS = 10      # timed repeats per workload: median, p10 and p90 are reported
+
+
+def graph_time_reps(torch, fn, stream, warmup: int, iters: int, reps: int) -> list:
+    """Capture fn() once as a HIP graph; time `reps` repeats of `iters` replays each (events
+    on `stream`) and return the mean ms per replay of every repeat."""
     with torch.cuda.stream(stream):
         fn()
     stream.synchronize()
@@ -193,14 +197,43 @@ def graph_time_ms(torch, fn, stream, warmup: int, iters: int) -> float:
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        for _ in range(iters):
-            graph.replay()
-        end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / iters
+    out = []
+    for _ in range(reps):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            for _ in range(iters):
+                graph.replay()
+            end.record(stream)
+        torch.cuda.synchronize()
+        out.append(start.elapsed_time(end) / iters)
+    return out
+
+
+def graph_time_ms(torch, fn, stream, warmup: int, iters: int) -> float:
+    """Capture fn() once as a HIP graph; return the mean ms per replay over `iters` replays."""
+    return graph_time_reps(torch, fn, stream, warmup, iters, 1)[0]
+
+
+def percentile(reps: list, f: float, scale: float = 1.0) -> float:
+    """The f-th percentile of per-repeat times divided by `scale` (linear interpolation
+    between order statistics)."""
+    v = sorted(m / scale for m in reps)
+    i = f / 100.0 * (len(v) - 1)
+    lo = int(i)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (i - lo)
+
+
+def median_of(reps: list, scale: float = 1.0) -> float:
+    return percentile(reps, 50, scale)
+
+
+def spread(reps: list, scale: float = 1.0) -> dict:
+    """Median, p10 and p90 of per-repeat times (ms, each divided by `scale`)."""
+    return {"repeats": len(reps), "ms_p10": round(percentile(reps, 10, scale), 6),
+            "ms_median": round(percentile(reps, 50, scale), 6),
+            "ms_p90": round(percentile(reps, 90, scale), 6)}
 
 
 def n_active(torch, ids) -> int:
@@ -235,10 +268,12 @@ def bench_toy(torch, M, S, dev, stream, iters, cpu):
 
     def one():
         M.moe_layer(tx, tG, None, ex, k, out, ws=ws, stream=stream)
-    ms = graph_time_ms(torch, one, stream, 3, max(iters, 20))
+    reps = graph_time_reps(torch, one, stream, 3, max(iters, 20), REPEATS)
+    ms = median_of(reps)
     r = {"workload": "toy layer: 16 tokens x d_model 256, 16 Q8_0 experts (256x128 / 128x256), "
                      "top-2, no bias (latency-bound; correctness config)",
-         "tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_call": round(ms, 5)}
+         "tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_call": round(ms, 5),
+         "spread": spread(reps)}
     if cpu:
         oex = O.Experts(lambda e: S.split_blob(blobs[e], Dm, Fm, S.FMT_Q8_0), S.FMT_Q8_0)
 
@@ -272,7 +307,8 @@ def bench_decode_batch(torch, M, S, dev, stream, iters, cpu):
             M.moe_layer(bufs[l], gates[l][0], gates[l][1], ex[l], K, bufs[l + 1],
                         flags=flags if l > 0 else M.F_RESIDUAL, topk_ids=ids[l], ws=ws,
                         stream=stream)
-    ms = graph_time_ms(torch, one, stream, 3, iters) / L4
+    reps = graph_time_reps(torch, one, stream, 3, iters, REPEATS)
+    ms = median_of(reps, L4)
     M.check_workspace(ws, stream=stream)
     U = sum(n_active(torch, ids[l]) for l in range(L4)) / L4
     nbytes = U * Q4_BLOB + GATE_BYTES + 2 * T * D * 4
@@ -281,6 +317,7 @@ def bench_decode_batch(torch, M, S, dev, stream, iters, cpu):
                      "16 distinct layers chained (residual + RMSNorm)",
          "tokens_per_s": round(T / (ms / 1e3), 1), "mean_active_experts": round(U, 2)}
     r.update(rates(ms, nbytes, flops))
+    r["spread"] = spread(reps, L4)
     r["traffic"] = counter_traffic("decode_batch_q4_layer", BATCH_SRCS)
     if cpu:
         def run(n):
@@ -337,9 +374,11 @@ def bench_prefill_down(torch, M, S, dev, stream, iters, cpu):
                 M.moe_group(ids[l], E, offs[l], rows[l], ws, stream=stream)
                 M.moe_expert_ffn(h, M.STAGE_DOWN, ex[l], ids[l], w[l], offs[l], rows[l],
                                  out=out, flags=fl, ws=ws, stream=stream)
-        ms = graph_time_ms(torch, one, stream, 3, iters) / L4
+        reps = graph_time_reps(torch, one, stream, 3, iters, REPEATS)
+        ms = median_of(reps, L4)
         r = {"tokens_per_s": round(T / (ms / 1e3), 1)}
         r.update(rates(ms, nbytes, flops))
+        r["spread"] = spread(reps, L4)
         res[name] = r
     res["traffic"] = counter_traffic("prefill_down_q4_operator", DOWN_OP_SRCS)
     if cpu:
@@ -382,7 +421,8 @@ def bench_prefill_stack(torch, M, S, dev, stream, arena, layers_np, gates, iters
                 M.moe_layer(src, gates[l][0], gates[l][1], ex[l], K, outs[l, sl],
                             flags=flags if l > 0 else M.F_RESIDUAL, topk_ids=ids[l, sl], ws=ws,
                             stream=stream)
-    ms = graph_time_ms(torch, one, stream, 2, iters)
+    reps = graph_time_reps(torch, one, stream, 2, iters, REPEATS)
+    ms = median_of(reps)
     M.check_workspace(ws, stream=stream)
     if not torch.isfinite(outs[L - 1]).all():
         raise RuntimeError("prefill stack: non-finite output")
@@ -397,6 +437,7 @@ def bench_prefill_stack(torch, M, S, dev, stream, arena, layers_np, gates, iters
     r.update(rates(ms, nbytes, flops))
     r["ms_per_call"] = round(ms / len(Us), 5)
     r["ms_per_pass"] = round(ms, 4)
+    r["spread"] = spread(reps)                      # ms per pass
     r["traffic_per_microbatch_layer"] = counter_traffic("prefill_layer_q8_0", PREFILL_SRCS)
     if cpu:
         # once: a 2-token sample (one from each microbatch) through all 48 layers
@@ -439,7 +480,8 @@ def bench_attn(torch, M, S, dev, stream, iters, cpu):
     def one():
         for l in range(L):
             M.moe_attn_prep(x, W[l], pos, q, kc[l], vc[l], ws=ws, stream=stream)
-    ms = graph_time_ms(torch, one, stream, 3, iters) / L
+    reps = graph_time_reps(torch, one, stream, 3, iters, REPEATS)
+    ms = median_of(reps, L)
     rb = Dm // 32 * 34
     nbytes = N * rb + Dm * 4 * 2 + 2 * hd * 4 + nq * hd * 4 + 2 * nkv * hd * 4 + 4
     r = {"workload": "attention-side primitives, one decode token: input RMSNorm, Q8_0 Q/K/V "
@@ -447,6 +489,7 @@ def bench_attn(torch, M, S, dev, stream, iters, cpu):
                      "append; 48 distinct layers",
          "us_per_call": round(ms * 1e3, 3)}
     r.update(rates(ms, nbytes, 2.0 * Dm * N))
+    r["spread"] = spread(reps, L)
     # fp32 vector dots, no matrix cores: the MFMA fields do not apply
     r.pop("mfma_tflops", None)
     r.pop("mfma_frac", None)
@@ -514,6 +557,8 @@ def main():
         M.moe_decode_stack(x0[0], stack_layers, K, outs, ws=ws, stream=stream)
 
     ms_step = graph_time_ms(torch, one_stack, stream, a.warmup, a.steps)
+    # spread: REPEATS further timed runs of steps/10 steps each, after the timed region
+    step_reps = graph_time_reps(torch, one_stack, stream, 0, max(1, a.steps // 10), REPEATS)
     M.check_workspace(ws, stream=stream)             # raises if an exchange wait gave up
     if not torch.isfinite(outs).all():
         raise RuntimeError("non-finite output")
@@ -546,6 +591,8 @@ def main():
             "launches_per_step": launches,
         },
         "hbm_gbps": round(achieved, 1),
+        "spread": dict(spread(step_reps), steps_per_repeat=max(1, a.steps // 10),
+                       note="ms per step over further repeats after the timed region"),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -569,7 +616,8 @@ def main():
                 M.moe_layer(bufs[l], gates[l][0], gates[l][1], experts[l], K, bufs[l + 1],
                             flags=flags if l > 0 else M.F_RESIDUAL, ws=ws, stream=stream)
 
-        ms_pl = graph_time_ms(torch, one_pass, stream, a.warmup, a.steps)
+        pl_reps = graph_time_reps(torch, one_pass, stream, a.warmup, max(1, a.steps // 10), REPEATS)
+        ms_pl = median_of(pl_reps)
         M.check_workspace(ws, stream=stream)
         diff = float((bufs[L][0] - outs[L - 1]).abs().max() / outs[L - 1].pow(2).mean().sqrt())
         extra["decode_per_layer"] = {
@@ -579,6 +627,7 @@ def main():
             "hbm_gbps": round(DECODE_ALGO_BYTES / (ms_pl / 1e3 / L) / 1e9, 1),
             "hbm_frac": round(DECODE_ALGO_BYTES / (ms_pl / 1e3 / L) / 1e9 / HBM_PEAK_GBPS, 4),
             "max_rel_diff_vs_stack": diff,
+            "spread": spread(pl_reps, L),
         }
         print(f"[bench] decode per layer: {ms_pl * 1e3 / L:.2f} us per layer call",
               file=sys.stderr, flush=True)
