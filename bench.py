@@ -268,7 +268,7 @@ def bench_toy(torch, M, S, dev, stream, iters, cpu):
 
     def one():
         M.moe_layer(tx, tG, None, ex, k, out, ws=ws, stream=stream)
-    reps = graph_time_reps(torch, one, stream, 3, max(iters, 20), REPEATS)
+    reps = graph_time_reps(torch, one, stream, 3, max(iters, 50), REPEATS)
     ms = median_of(reps)
     r = {"workload": "toy layer: 16 tokens x d_model 256, 16 Q8_0 experts (256x128 / 128x256), "
                      "top-2, no bias (latency-bound; correctness config)",
