@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=48)
+    ap.add_argument("--repeats", type=int, default=10,
+                    help="timed repeats per workload (median, p10, p90); 1 for profiler runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle time budget of the headline's cpu_baseline")
@@ -519,6 +521,8 @@ def lazy_layer(arena_l):
 
 def main():
     a = parse()
+    global REPEATS
+    REPEATS = max(1, a.repeats)
     if a.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; runs on more than one GPU are "
                                    "not part of it (the sharding plan is documented, not run)"}))
