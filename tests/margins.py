@@ -3,8 +3,8 @@
 Every element-wise comparison against the oracle records its max|GPU - oracle| /
 RMS(oracle) here under the running test's name; the conftest prints the worst
 value per test in pytest's terminal summary (shown also with -q) and writes them
-to gpurun_out/gpu_margins.json, so a margin creeping toward the 2e-3 bound is
-visible in every run, not only when a test fails.
+to gpu_margins.json in the run-output folder, so a margin creeping toward the
+2e-3 bound is visible in every run, not only when a test fails.
 """
 from __future__ import annotations
 
