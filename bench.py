@@ -524,7 +524,7 @@ def main():
     global REPEATS
     REPEATS = max(1, a.repeats)
     if a.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; runs on more than one GPU are "
+        print(json.dumps({"error": "bench.py measures one GPU; runs on more than one GPU are "
                                    "not part of it (the sharding plan is documented, not run)"}))
         sys.exit(2)
     import torch
