@@ -79,8 +79,9 @@ enum {
   MOE_E_HIP = 7,         /* a HIP launch failed                                   */
   MOE_E_TIMEOUT = 8,     /* moe_workspace_status: a fused kernel's bounded wait   */
                          /* gave up since the word was last cleared               */
-  MOE_E_RANGE = 9        /* moe_workspace_status: a fused decode stack met a value */
+  MOE_E_RANGE = 9,       /* moe_workspace_status: a fused decode stack met a value */
                          /* outside its fixed-point range (outputs hold NaN)      */
+  MOE_E_OVERLAP = 10     /* an output buffer overlaps an input buffer            */
 };
 
 enum { MOE_FMT_Q8_0 = 0, MOE_FMT_Q4 = 1 };
@@ -174,7 +175,9 @@ moe_status moe_group(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
  *   y   [T*k][D] fp32 flat (t, j) order, or NULL;
  *   out [T][D] fp32 = sum_j topk_w[t][j] y_{t*k+j} (+ x_t with MOE_F_RESIDUAL,
  *     stage FULL only), or NULL.  At least one of y / out is non-NULL.
- *   expert_offsets / sorted_rows come from moe_group on the same ids. */
+ *   expert_offsets / sorted_rows come from moe_group on the same ids.
+ *   y and out must not overlap `in` or each other (MOE_E_OVERLAP, checked on
+ *   the host before anything is enqueued). */
 moe_status moe_expert_ffn(const float* in, int32_t stage, const moe_experts* W /* host */,
                           const int32_t* topk_ids, const float* topk_w,
                           const int32_t* expert_offsets, const int32_t* sorted_rows, int64_t T,
@@ -196,6 +199,8 @@ moe_status moe_combine(const float* y, const float* topk_w, int64_t T, int32_t k
  *   MOE_F_RESIDUAL out = u + MoE(u), else out = MoE(u).
  *   topk_ids, topk_w, expert_offsets, sorted_rows: optional outputs (NULL =
  *   kept in the workspace only).
+ *   out must not overlap x: workgroups still reading x could see outputs
+ *   (MOE_E_OVERLAP, checked on the host before anything is enqueued).
  * One token at the tuned geometry (D 2048, F 768, E 128, k 8, 16-byte aligned
  * weight bases and strides, x and out) runs as one launch of the decode-stack
  * kernel (see moe_decode_stack: bit-reproducible, fixed-point sums, the same
@@ -254,7 +259,8 @@ typedef struct {
  * are NaN and moe_workspace_status reports MOE_E_RANGE.  Other shapes run
  * moe_layer per layer.
  *   x [D] fp32 (one token); layers: host array of num_layers >= 1 entries;
- *   outs [num_layers][D] fp32: o_l of every layer;
+ *   outs [num_layers][D] fp32: o_l of every layer; must not overlap x
+ *   (MOE_E_OVERLAP);
  *   topk_ids [num_layers][k] int32, topk_w [num_layers][k] fp32: optional
  *   (NULL) routing of every layer, as moe_route reports it.
  *   flags: MOE_F_PRENORM or 0 (MOE_F_RESIDUAL and MOE_F_DETERMINISTIC are

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 MOE_OK = 0
 MOE_E_TIMEOUT = 8
 MOE_E_RANGE = 9
+MOE_E_OVERLAP = 10
 FMT_Q8_0, FMT_Q4 = 0, 1
 STAGE_FULL, STAGE_DOWN = 0, 1
 F_RESIDUAL, F_DETERMINISTIC, F_PRENORM, F_FP16_ACT, F_BANDED = 1, 2, 4, 8, 16

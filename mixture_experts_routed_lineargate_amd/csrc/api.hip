@@ -93,6 +93,12 @@ static moe_status check_gate_up(const moe_experts* W) {
     if ((expr) != hipSuccess) return MOE_E_HIP; \
   } while (0)
 
+// The byte ranges [a, a + na) and [b, b + nb) share a byte.
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
+}
+
 // Route into the given outputs (ids / w must be device buffers of T*k).
 static moe_status do_route(const float* x, int64_t T, int D, const float* G, const float* bias,
                            int E, int k, int32_t* ids, float* w, const Workspace& ws,
@@ -292,6 +298,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_E_HIP: return "HIP launch failed";
     case MOE_E_TIMEOUT: return "a bounded exchange wait gave up (outputs hold NaN)";
     case MOE_E_RANGE: return "a decode-stack value outside the fixed-point range (outputs hold NaN)";
+    case MOE_E_OVERLAP: return "an output buffer overlaps an input buffer";
     default: return "unknown status";
   }
 }
@@ -357,6 +364,14 @@ moe_status moe_expert_ffn(const float* in, int32_t stage, const moe_experts* W,
   const size_t need =
       moe_workspace_bytes(T, W->d_model, W->d_ff, W->num_experts, k, W->format, flags);
   if (!ws || ws_bytes < need) return MOE_E_WORKSPACE;
+  {
+    const size_t rows = (size_t)T * (stage == MOE_STAGE_FULL ? 1 : k);
+    const size_t in_b = rows * (stage == MOE_STAGE_FULL ? W->d_model : W->d_ff) * 4;
+    if ((out && overlaps(in, in_b, out, (size_t)T * W->d_model * 4)) ||
+        (y && overlaps(in, in_b, y, (size_t)T * k * W->d_model * 4)) ||
+        (y && out && overlaps(y, (size_t)T * k * W->d_model * 4, out, (size_t)T * W->d_model * 4)))
+      return MOE_E_OVERLAP;
+  }
   const Workspace w = carve_workspace(ws, T, W->d_model, W->d_ff, W->num_experts, k, flags);
   return do_ffn(in, stage, to_dev(*W), topk_ids, topk_w, expert_offsets, sorted_rows, T, k, y, out,
                 flags, w, (hipStream_t)stream);
@@ -392,6 +407,7 @@ moe_status moe_layer(const float* x, const float* gate, const float* bias, const
     return MOE_E_ALIGN;
   const size_t need = moe_workspace_bytes(T, D, F, E, k, W->format, flags);
   if (!ws || ws_bytes < need) return MOE_E_WORKSPACE;
+  if (overlaps(x, (size_t)T * D * 4, out, (size_t)T * D * 4)) return MOE_E_OVERLAP;
   return layer_impl(x, gate, bias, W, T, k, flags, out, topk_ids, topk_w, expert_offsets,
                     sorted_rows, ws, (hipStream_t)stream);
 }
@@ -416,6 +432,7 @@ moe_status moe_layer_noalloc(const float* x, const float* gate, const float* bia
               (long long)T, NOALLOC_SCRATCH_BYTES);
     return MOE_E_UNSUPPORTED;
   }
+  if (overlaps(x, (size_t)T * D * 4, out, (size_t)T * D * 4)) return MOE_E_OVERLAP;
   hipStream_t s = (hipStream_t)stream;
   void* ws = nullptr;
   MOE_TRY(scratch_for_device(s, &ws));
@@ -452,6 +469,7 @@ moe_status moe_decode_stack(const float* x, int32_t num_layers, const moe_stack_
     need = n > need ? n : need;
   }
   if (!ws || ws_bytes < need) return MOE_E_WORKSPACE;
+  if (overlaps(x, (size_t)D * 4, outs, (size_t)num_layers * D * 4)) return MOE_E_OVERLAP;
   hipStream_t s = (hipStream_t)stream;
   const Workspace w = carve_workspace(ws, 1, D, F, E, k, MOE_F_PRENORM | MOE_F_RESIDUAL);
 

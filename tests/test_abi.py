@@ -34,10 +34,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(10):
+    for s in range(11):
         assert M.status_str(s) != "unknown status"
     assert M.status_str(0) == "ok"
-    assert M.status_str(10) == "unknown status"
+    assert M.status_str(11) == "unknown status"
 
 
 def test_workspace_bytes():
@@ -93,6 +93,7 @@ def test_layer_rejects_bad_arguments():
     assert _layer(ex, ws=None) == 5
     assert _layer(ex, ws_bytes=1000) == 5
     assert _layer(ex, T=0) == 0          # empty input: nothing enqueued
+    assert _layer(ex, out=FAKE + 4 * 4 * 2048 - 4) == M.MOE_E_OVERLAP   # last x row meets out
 
 
 def test_route_group_combine_validation():
@@ -119,6 +120,8 @@ def test_expert_ffn_validation():
     assert args(y=None, out=None) == 1
     assert args(y=None, out=FAKE, w=None) == 1
     assert args(ws=None) == 5
+    assert args(y=FAKE + 4096) == M.MOE_E_OVERLAP                        # y inside x
+    assert args(y=None, out=FAKE + 4 * 2048 * 4 - 4) == M.MOE_E_OVERLAP  # out meets x
     down_only = _experts(w_gate=None, w_up=None)
     assert L.moe_expert_ffn(FAKE, 0, ctypes.byref(down_only), FAKE, FAKE, FAKE, FAKE, 4, 8, FAKE,
                             None, 0, FAKE, 1 << 40, None) == 1
@@ -141,6 +144,7 @@ def test_layer_noalloc_validation():
     assert call(e=_experts(format=9)) == 4
     assert call(T=64) == 6                      # > 8 MiB of workspace at this geometry
     assert call(T=1024) == 6
+    assert call(out=FAKE + 16) == M.MOE_E_OVERLAP
     assert L.moe_workspace_bytes(32, 2048, 768, 128, 8, 1, M.F_PRENORM) <= 8 << 20
     assert L.moe_workspace_bytes(64, 2048, 768, 128, 8, 1, 0) > 8 << 20
 
@@ -210,3 +214,4 @@ def test_decode_stack_validation():
     assert call(lay=layers(ex, _experts(d_ff=1536))) == 2
     assert call(lay=layers(ex, _experts(format=3))) == 4
     assert call(n=1, lay=layers(ex, gate=None)) == 1
+    assert call(outs=FAKE - 2048 * 4) == M.MOE_E_OVERLAP                # x is o_1
