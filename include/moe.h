@@ -308,6 +308,7 @@ size_t moe_attn_workspace_bytes(int64_t T, const moe_attn_weights* W /* host */)
  *   q [T][Hq][hd] gets the rotated q; k_cache and v_cache ([max_pos][Hkv][hd]
  *   fp32, caller-owned) get the rotated k and the projected v at row pos[t].
  *   A token whose pos is outside [0, max_pos) writes q only.
+ *   x, q, k_cache and v_cache must not overlap (MOE_E_OVERLAP).
  * Causal attention itself (scores, softmax, value aggregation, output
  * projection) is not part of this call.  x [T][D] 16-byte aligned; pos [T]
  * int32; ws at least moe_attn_workspace_bytes, zero-filled before first use,

@@ -553,6 +553,14 @@ moe_status moe_attn_prep(const float* x, int64_t T, const moe_attn_weights* W, c
     return MOE_E_ALIGN;
   const size_t need = moe_attn_workspace_bytes(T, W);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return MOE_E_WORKSPACE;
+  {
+    const size_t xb = (size_t)T * D * 4, qb = (size_t)T * Hq * hd * 4;
+    const size_t cb = (size_t)max_pos * Hkv * hd * 4;
+    if (overlaps(x, xb, q, qb) || overlaps(x, xb, k_cache, cb) || overlaps(x, xb, v_cache, cb) ||
+        overlaps(q, qb, k_cache, cb) || overlaps(q, qb, v_cache, cb) ||
+        overlaps(k_cache, cb, v_cache, cb))
+      return MOE_E_OVERLAP;
+  }
   trace("attn prep", T, D, hd, Hq, Hkv, W->format);
   if (launch_attn_prep(x, T, D, W->attn_gain, (const uint8_t*)W->w_qkv, W->format, Hq, Hkv, hd,
                        W->q_gain, W->k_gain, pos, rope_theta, eps, q, k_cache, v_cache, max_pos,

@@ -174,6 +174,7 @@ def test_attn_prep_validation():
     assert call(w=W(w_qkv=None)) == 1
     assert call(x=FAKE + 4) == 3
     assert call(wsb=100) == 5
+    assert call() == M.MOE_E_OVERLAP        # x, q and both caches share one address here
 
 
 def test_workspace_status_validation():
