@@ -186,7 +186,8 @@ moe_status moe_expert_ffn(const float* in, int32_t stage, const moe_experts* W /
 
 /* Weighted combine (technical-overview page: "weighted combine").
  *   out[t] = sum_{j<k} topk_w[t][j] * y[t*k+j] (+ residual[t] when non-NULL),
- *   summed in j order.  y [T*k][D], out [T][D]. */
+ *   summed in j order.  y [T*k][D], out [T][D].  out may be residual itself
+ *   (in place); any other overlap of out with an input is MOE_E_OVERLAP. */
 moe_status moe_combine(const float* y, const float* topk_w, int64_t T, int32_t k, int32_t D,
                        const float* residual, float* out, void* stream);
 

@@ -385,6 +385,14 @@ moe_status moe_combine(const float* y, const float* topk_w, int64_t T, int32_t k
   if (!aligned(y, 4) || !aligned(topk_w, 4) || !aligned(out, 4) ||
       (residual && !aligned(residual, 4)))
     return MOE_E_ALIGN;
+  {
+    // out may be the residual itself (each element is read before it is written by
+    // the same thread), but no other overlap
+    const size_t ob = (size_t)T * D * 4;
+    if (overlaps(y, (size_t)T * k * D * 4, out, ob) || overlaps(topk_w, (size_t)T * k * 4, out, ob) ||
+        (residual && residual != out && overlaps(residual, ob, out, ob)))
+      return MOE_E_OVERLAP;
+  }
   trace("combine", T, D, 0, 0, k, -1);
   if (launch_combine(y, topk_w, T, k, D, residual, out, (hipStream_t)stream) != hipSuccess)
     return MOE_E_HIP;

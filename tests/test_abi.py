@@ -107,6 +107,10 @@ def test_route_group_combine_validation():
     assert L.moe_group(FAKE, 0, 2, 8, FAKE, FAKE, None, 0, None) == 0
     assert L.moe_combine(FAKE, FAKE, 4, 0, 2048, None, FAKE, None) == 2
     assert L.moe_combine(FAKE, None, 4, 8, 2048, None, FAKE, None) == 1
+    far = FAKE + (1 << 32)
+    assert L.moe_combine(FAKE, far, 4, 8, 2048, None, FAKE + 4096, None) == M.MOE_E_OVERLAP
+    assert L.moe_combine(FAKE, far, 4, 8, 2048, far + (1 << 20) + 4, far + (1 << 20), None) == \
+        M.MOE_E_OVERLAP                                                   # shifted residual
     assert L.moe_rmsnorm(FAKE, 4, 2048, -1.0, FAKE, None) == 2
     assert L.moe_rmsnorm(FAKE, 0, 2048, 1e-6, FAKE, None) == 0
 
